@@ -1,0 +1,178 @@
+"""ctypes wrapper of the fp64 CPU oracle (``oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the
+benchmark's CPU-baseline leg are the only callers. Product code never
+imports this package, and the GPU path shares no code with it.
+
+Inputs are numpy ``uint16`` arrays holding fp16/bf16 bit patterns (as made
+by :mod:`synth`); outputs are float64 arrays.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+# A test may point the wrapper at a deliberately mutated build of oracle.c to
+# show that the pins catch the mutation; nothing else sets this.
+_LIB_OVERRIDE = os.environ.get("NORM_GEMM_ORACLE_LIB")
+
+F16, BF16 = 0, 1
+NORM_NONE, NORM_LAYERNORM, NORM_RMSNORM = 0, 1, 2
+ACT_NONE, ACT_SILU = 0, 1
+
+
+def build(force: bool = True) -> str:
+    """Compile ``oracle.c`` with gcc (portable x86-64 code, OpenMP)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+               "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        path = _LIB_OVERRIDE or _LIB
+        if not _LIB_OVERRIDE and not os.path.exists(_LIB):
+            build(force=False)
+        L = ctypes.CDLL(path)
+        p16 = ctypes.POINTER(ctypes.c_uint16)
+        pi64 = ctypes.POINTER(ctypes.c_int64)
+        pf64 = ctypes.POINTER(ctypes.c_double)
+        i64 = ctypes.c_int64
+        L.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
+        L.oracle_f16_to_f64.restype = ctypes.c_double
+        L.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
+        L.oracle_bf16_to_f64.restype = ctypes.c_double
+        L.oracle_num_threads.restype = ctypes.c_int
+        L.oracle_normalize.argtypes = [p16, p16, p16, i64, i64, ctypes.c_float,
+                                       ctypes.c_int, ctypes.c_int, pi64, i64, pf64]
+        L.oracle_normalize.restype = ctypes.c_int
+        L.oracle_norm_gemm.argtypes = [p16, p16, p16, p16, p16, i64, i64, i64,
+                                       ctypes.c_float, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_int, pi64, i64, pi64, i64, pf64]
+        L.oracle_norm_gemm.restype = ctypes.c_int
+        L.oracle_ffn.argtypes = [p16, p16, p16, p16, p16, p16, p16, i64, i64, i64,
+                                 i64, ctypes.c_float, ctypes.c_int, ctypes.c_int,
+                                 ctypes.c_int, pi64, i64, pi64, i64, pf64]
+        L.oracle_ffn.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _u16(a: Optional[np.ndarray]):
+    if a is None:
+        return None, None
+    a = np.ascontiguousarray(a, dtype=np.uint16)
+    return a, a.ctypes.data_as(ctypes.POINTER(ctypes.c_uint16))
+
+
+def _idx(ix: Optional[Sequence[int]], n: int):
+    arr = np.arange(n, dtype=np.int64) if ix is None else np.ascontiguousarray(ix, dtype=np.int64)
+    return arr, arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+
+
+def num_threads() -> int:
+    return int(lib().oracle_num_threads())
+
+
+def f16_to_f64(bits: int) -> float:
+    return lib().oracle_f16_to_f64(int(bits))
+
+
+def bf16_to_f64(bits: int) -> float:
+    return lib().oracle_bf16_to_f64(int(bits))
+
+
+def decode(bits: np.ndarray, dtype: int) -> np.ndarray:
+    """Decode an array of 16-bit patterns with the oracle's own decoder."""
+    f = lib().oracle_bf16_to_f64 if dtype == BF16 else lib().oracle_f16_to_f64
+    flat = np.asarray(bits, dtype=np.uint16).ravel()
+    table = np.array([f(i) for i in range(65536)], dtype=np.float64)
+    return table[flat].reshape(np.shape(bits))
+
+
+def normalize(x, gamma, beta, eps: float, norm: int, dtype: int,
+              rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    M, K = x.shape
+    x, px = _u16(x)
+    g, pg = _u16(gamma)
+    b, pb = _u16(beta)
+    r, pr = _idx(rows, M)
+    out = np.empty((len(r), K), dtype=np.float64)
+    rc = lib().oracle_normalize(px, pg, pb, M, K, eps, norm, dtype, pr, len(r),
+                                out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
+    if rc != 0:
+        raise ValueError(f"oracle_normalize failed ({rc})")
+    return out
+
+
+def norm_gemm(x, gamma, beta, W, bias, eps: float, norm: int, act: int, dtype: int,
+              rows: Optional[Sequence[int]] = None,
+              cols: Optional[Sequence[int]] = None) -> np.ndarray:
+    M, K = x.shape
+    N = W.shape[0]
+    assert W.shape[1] == K
+    x, px = _u16(x)
+    g, pg = _u16(gamma)
+    b, pb = _u16(beta)
+    w, pw = _u16(W)
+    bi, pbi = _u16(bias)
+    r, pr = _idx(rows, M)
+    c, pc = _idx(cols, N)
+    out = np.empty((len(r), len(c)), dtype=np.float64)
+    rc = lib().oracle_norm_gemm(px, pg, pb, pw, pbi, M, N, K, eps, norm, act, dtype,
+                                pr, len(r), pc, len(c),
+                                out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
+    if rc != 0:
+        raise ValueError(f"oracle_norm_gemm failed ({rc})")
+    return out
+
+
+def ffn(x, gamma, beta, W1, b1, W2, b2, eps: float, norm: int, act: int, dtype: int,
+        rows: Optional[Sequence[int]] = None,
+        cols: Optional[Sequence[int]] = None) -> np.ndarray:
+    M, K = x.shape
+    F = W1.shape[0]
+    N = W2.shape[0]
+    assert W1.shape[1] == K and W2.shape[1] == F
+    x, px = _u16(x)
+    g, pg = _u16(gamma)
+    b, pb = _u16(beta)
+    w1, pw1 = _u16(W1)
+    bb1, pb1 = _u16(b1)
+    w2, pw2 = _u16(W2)
+    bb2, pb2 = _u16(b2)
+    r, pr = _idx(rows, M)
+    c, pc = _idx(cols, N)
+    out = np.empty((len(r), len(c)), dtype=np.float64)
+    rc = lib().oracle_ffn(px, pg, pb, pw1, pb1, pw2, pb2, M, K, F, N, eps, norm, act,
+                          dtype, pr, len(r), pc, len(c),
+                          out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
+    if rc != 0:
+        raise ValueError(f"oracle_ffn failed ({rc})")
+    return out
+
+
+def run_case(case, rows=None, cols=None) -> np.ndarray:
+    """Oracle output for a :class:`synth.Case` (optionally a row/col sample)."""
+    A = case.arrays
+    if case.kind == "ffn":
+        return ffn(A["x"], A.get("gamma"), A.get("beta"), A["W1"], A.get("b1"),
+                   A["W2"], A.get("b2"), case.eps, case.norm, case.act, case.dtype,
+                   rows, cols)
+    return norm_gemm(A["x"], A.get("gamma"), A.get("beta"), A["W"], A.get("bias"),
+                     case.eps, case.norm, case.act, case.dtype, rows, cols)

@@ -1,0 +1,52 @@
+"""Plant plausible mistakes in a copy of the oracle and check the pins fail.
+
+Each mutation is a one-line textual change to ``oracle/oracle.c`` compiled
+into a temporary library on the CPU; the pin suite is then run against that
+library in a subprocess and must fail. The committed oracle is not touched.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "oracle.c")
+
+MUTATIONS = {
+    "eps_outside_root": ("r = 1.0 / sqrt(var + eps);", "r = 1.0 / (sqrt(var) + eps);"),
+    "unbiased_variance": ("double var = q / (double)K;",
+                          "double var = q / (double)(K > 1 ? K - 1 : 1);"),
+    "dropped_beta": ("a[k] = a[k] * g + b;", "a[k] = a[k] * g + 0.0 * b;"),
+    "ignored_gamma": ("double g = gamma ? dec(gamma[k], dtype) : 1.0;", "double g = 1.0;"),
+    "mean_sign": ("a[k] = (a[k] - mu) * r;", "a[k] = (a[k] + mu) * r;"),
+    "rms_without_eps": ("r = 1.0 / sqrt(ms + eps);", "r = 1.0 / sqrt(ms);"),
+    "transposed_weight": ("z += ar[k] * dec(wr[k], dtype);",
+                          "z += ar[k] * dec(W[(k * N + cols[j]) % (N * K)], dtype);"),
+    "bias_after_act": ("y_out[t] = apply_act(z, act);",
+                       "y_out[t] = apply_act(z - (bias ? dec(bias[cols[j]], dtype) : 0.0), act)"
+                       " + (bias ? dec(bias[cols[j]], dtype) : 0.0);"),
+    "silu_sign": ("return z / (1.0 + exp(-z));", "return z / (1.0 + exp(z));"),
+    "ffn_h_not_activated": ("h[f] = apply_act(z, act);", "h[f] = z;"),
+    "f16_exponent_bias": ("v = ldexp(1.0 + (double)f / 1024.0, e - 15);",
+                          "v = ldexp(1.0 + (double)f / 1024.0, e - 16);"),
+    "bf16_fraction": ("v = ldexp(1.0 + (double)f / 128.0, e - 127);",
+                      "v = ldexp(1.0 + (double)f / 256.0, e - 127);"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    old, new = MUTATIONS[name]
+    src = open(SRC, encoding="utf-8").read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not found exactly once"
+    mutated = tmp_path / "oracle_mut.c"
+    mutated.write_text(src.replace(old, new), encoding="utf-8")
+    lib = tmp_path / "liboracle_mut.so"
+    subprocess.run(["gcc", "-O1", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-o",
+                    str(lib), str(mutated), "-lm"], check=True)
+    env = dict(os.environ, NORM_GEMM_ORACLE_LIB=str(lib), OMP_NUM_THREADS="2")
+    res = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                          os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                         cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert res.returncode != 0, f"pins did not catch mutation {name}:\n{res.stdout[-2000:]}"
