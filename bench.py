@@ -1,0 +1,219 @@
+#!/usr/bin/env python3
+"""Benchmark of the normalization-prologue GEMM on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one call of the hot path on one batch of synthetic input that is
+already resident in device memory. The default workload is LayerNorm +
+Linear + bias on x[1024, 8192] (batch 8 x seq 128) and W[8192, 8192] in fp16.
+W is rotated over several device copies so that timed calls stream it from
+HBM instead of the 256 MB last-level cache.
+
+Prints ONE JSON line with the throughput, a roofline object for the kernel
+(algorithmic FLOPs or bytes per launch over the average launch duration,
+measured with HIP events on the launch stream) and the fp64 CPU oracle timed
+on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused norm+GEMM+SiLU TFLOP/s & % MFMA peak; decode GB/s & % HBM peak"
+PEAK_MFMA_F16_TFLOPS = 2516.6   # 256 CUs x 2.4 GHz x 4096 dense fp16/bf16 FLOP/clk/CU
+PEAK_HBM_GBS = 8000.0           # HBM3E, 8 TB/s
+LLC_BYTES = 256 << 20           # Infinity Cache (MALL)
+
+
+def workload(name: str):
+    import synth
+    if name not in synth.WORKLOADS:
+        raise SystemExit(f"unknown workload {name!r}; choose from {sorted(synth.WORKLOADS)}")
+    return synth.WORKLOADS[name](seed=0)
+
+
+def upload(bits, dtype, device):
+    """uint16 bit patterns -> fp16/bf16 device tensor with the same bits."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.float16 if dtype == 0 else torch.bfloat16).to(device)
+
+
+def algorithmic(case):
+    """FLOPs (2 per multiply-add of every GEMM) and bytes (each input and the
+    output read or written once; the FFN's intermediate h is not counted)."""
+    M, K, N = case.M, case.K, case.N
+    nbytes = sum(int(a.size) * 2 for a in case.arrays.values() if a is not None)
+    if case.kind == "ffn":
+        F = case.F
+        return 2 * M * K * F + 2 * M * F * N, nbytes + M * N * 2
+    return 2 * M * N * K, nbytes + M * N * 2
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="ln_linear_bias_1024x8192")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle timing (e.g. under a profiler)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              f"(got --gpus {args.gpus}).", file=sys.stderr)
+        return 2
+
+    import torch
+    import norm_gemm_amd as ng
+
+    case = workload(args.workload)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    A = case.arrays
+    flops, nbytes = algorithmic(case)
+    is_ffn = case.kind == "ffn"
+    wkeys = ("W1", "W2") if is_ffn else ("W",)
+    wbytes = sum(A[k].size * 2 for k in wkeys)
+    copies = max(2, math.ceil(1.5 * LLC_BYTES / wbytes) + 1)
+    up = {k: upload(v, case.dtype, dev) for k, v in A.items() if v is not None and k not in wkeys}
+    wsets = []
+    base = {k: upload(A[k], case.dtype, dev) for k in wkeys}
+    for c in range(copies):
+        wsets.append({k: (base[k] if c == 0 else base[k].clone()) for k in wkeys})
+    get = lambda k: up.get(k)
+    out = torch.empty(case.M, case.N, dtype=up["x"].dtype, device=dev)
+    ws = None
+    if is_ffn:
+        ws = torch.empty(ng.fused_ffn_workspace_size(case.M, case.F, up["x"].dtype),
+                         dtype=torch.uint8, device=dev)
+
+    def step(i):
+        w = wsets[i % copies]
+        if is_ffn:
+            ng.fused_ffn(get("x"), w["W1"], w["W2"], get("gamma"), get("beta"), get("b1"),
+                         get("b2"), eps=case.eps, norm=case.norm, act=case.act,
+                         workspace=ws, out=out)
+        else:
+            ng.fused_norm_gemm(get("x"), w["W"], get("gamma"), get("beta"), get("bias"),
+                               eps=case.eps, norm=case.norm, act=case.act, out=out)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t_all0, t_all1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_all0.record(stream)
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    t_all1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_all0.elapsed_time(t_all1)
+    per_launch = np.array([a.elapsed_time(b) for a, b in ev])
+    ms_per_step = total_ms / args.steps
+    avg_launch_ms = float(per_launch.mean())
+
+    decode = case.M <= 32
+    if decode:
+        value = nbytes / (ms_per_step * 1e-3) / 1e9
+        unit = "GB/s"
+        achieved = nbytes / (avg_launch_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
+    else:
+        value = flops / (ms_per_step * 1e-3) / 1e12
+        unit = "TFLOP/s"
+        achieved = flops / (avg_launch_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_MFMA_F16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_MFMA_F16_TFLOPS, 4),
+                "traffic": None}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(case, args.cpu_seconds, decode)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16" if case.dtype == 0 else "bf16",
+        "data": "synthetic (seeded PCG64 normals; W rotated over %d device copies)" % copies,
+        "config": {"workload": case.name, "M": case.M, "K": case.K, "N": case.N,
+                   **({"F": case.F} if is_ffn else {}),
+                   "norm": ["none", "layernorm", "rmsnorm"][case.norm],
+                   "act": ["none", "silu"][case.act],
+                   "bias": (A.get("bias") is not None) or (A.get("b1") is not None),
+                   "eps": case.eps, "launches_per_step": 2 if is_ffn else 1},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "timing": {"avg_launch_ms": round(avg_launch_ms, 5),
+                   "p10_launch_ms": round(float(np.percentile(per_launch, 10)), 5),
+                   "p50_launch_ms": round(float(np.percentile(per_launch, 50)), 5),
+                   "p90_launch_ms": round(float(np.percentile(per_launch, 90)), 5),
+                   "host_wall_s": round(wall, 4)},
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def cpu_baseline(case, seconds: float, decode: bool):
+    """The fp64 oracle as it stands, on whole output rows of the workload,
+    doubling the row count until about `seconds` of wall time are spent."""
+    import oracle
+    done_rows = 0
+    spent = 0.0
+    batch = 1
+    row = 0
+    while spent < seconds and row < case.M:
+        rows = list(range(row, min(case.M, row + batch)))
+        t0 = time.perf_counter()
+        oracle.run_case(case, rows=rows)
+        spent += time.perf_counter() - t0
+        done_rows += len(rows)
+        row += len(rows)
+        batch *= 2
+    flops, nbytes = algorithmic(case)
+    frac = done_rows / case.M
+    if decode:
+        # the oracle streams all of W for every row, so its rate is reported
+        # as the workload's algorithmic bytes scaled by the rows completed
+        value = nbytes * frac / spent / 1e9
+        unit = "GB/s"
+    else:
+        value = flops * frac / spent / 1e12
+        unit = "TFLOP/s"
+    return {"value": round(value, 6), "unit": unit, "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{done_rows} of {case.M} output rows (all {case.N} columns), "
+                      f"{spent:.1f} s, fp64"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,112 @@
+/*
+ * norm_gemm.h -- C ABI of the MI355X (gfx950) normalization-prologue GEMM.
+ *
+ * Operation (page "LayerNorm 融合算子如何让大模型推理再快 15%？深度拆解 ATB 的实现",
+ * sections 1.1 and 2.1; page "昇腾CANN的MatMul融合玩法，让大模型推理快3倍",
+ * section 二, strategies 1-3):
+ *
+ *     a[m,:] = norm_affine(x[m,:])          LayerNorm, RMSNorm or none
+ *     y[m,n] = act( sum_k a[m,k] * W[n,k] + bias[n] )
+ *
+ * LayerNorm: a = (x - mean) / sqrt(var + eps) * gamma + beta with the biased
+ * variance; RMSNorm: a = x / sqrt(mean(x^2) + eps) * gamma (+ beta if given).
+ * Row statistics are reduced in fp32 in one pass (sum and sum of squares of
+ * the row shifted by its first element); the normalize + affine runs in fp32
+ * and is rounded once (round-to-nearest-even) to the operand type. The
+ * normalized activation exists only in on-chip memory and registers: it is
+ * never written to device memory. Products accumulate in fp32; the epilogue
+ * adds bias, applies the activation in fp32 and rounds once to the output
+ * type. act = SiLU is z / (1 + exp(-z)).
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are caller-owned DEVICE memory on the current HIP
+ *    device, contiguous row-major, one dtype (fp16 or bf16) for x, gamma,
+ *    beta, W, bias and y. x is [M,K], W is [N,K] (K contiguous, the "w.T"
+ *    convention of the pages), gamma/beta are [K], bias is [N], y is [M,N].
+ *  - Pointers must be at least 2-byte aligned; 16-byte aligned pointers with
+ *    K % 8 == 0 take 128-bit loads, anything else uses element loads in the
+ *    same kernels. Any M, N, K >= 1 is supported.
+ *  - gamma == NULL means gamma = 1; beta == NULL means beta = 0; bias == NULL
+ *    means no bias. With norm == NG_NORM_NONE, gamma, beta and eps are ignored.
+ *  - y is overwritten, never accumulated into. y must not overlap any input.
+ *  - stream is a hipStream_t (NULL = the null stream). Work is enqueued on it
+ *    and the call returns without synchronizing. Nothing is allocated, no
+ *    global state is kept; calls are re-entrant and thread-safe.
+ *  - On any validation error no kernel is launched and y is untouched. A
+ *    launch failure reports NG_ERR_HIP. Faults inside a kernel surface, as in
+ *    HIP, at the caller's next synchronization.
+ *  - There is no silent fallback to unfused operators: unsupported requests
+ *    return an error code.
+ */
+#ifndef NORM_GEMM_H
+#define NORM_GEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NORM_GEMM_ABI_VERSION 1
+
+typedef enum { NG_NORM_NONE = 0, NG_NORM_LAYERNORM = 1, NG_NORM_RMSNORM = 2 } ng_norm_t;
+typedef enum { NG_ACT_NONE = 0, NG_ACT_SILU = 1 } ng_act_t;
+typedef enum { NG_DTYPE_F16 = 0, NG_DTYPE_BF16 = 1 } ng_dtype_t;
+
+typedef enum {
+    NG_OK = 0,
+    NG_ERR_NULL = -1,         /* a required pointer is NULL                      */
+    NG_ERR_SHAPE = -2,        /* M, N, K or F < 1, or a size overflows int64      */
+    NG_ERR_ENUM = -3,         /* norm, act or dtype out of range                  */
+    NG_ERR_EPS = -4,          /* eps is NaN, infinite or negative                 */
+    NG_ERR_ALIAS = -5,        /* the output overlaps an input (or the workspace) */
+    NG_ERR_WORKSPACE = -6,    /* workspace missing or smaller than required       */
+    NG_ERR_UNSUPPORTED = -7,  /* no kernel for this request                       */
+    NG_ERR_ALIGN = -8,        /* a pointer is not 2-byte aligned                  */
+    NG_ERR_HIP = -9           /* the HIP runtime reported an error                */
+} ng_status_t;
+
+/*
+ * fused_norm_gemm: y[M,N] = act( norm_affine(x)[M,K] . W[N,K]^T + bias[N] ).
+ * One kernel launch. M <= 32 runs the skinny (decode) kernel that streams W
+ * once; larger M runs the tiled MFMA kernel. Returns an ng_status_t.
+ */
+int fused_norm_gemm(const void *x, const void *gamma, const void *beta,
+                    const void *W, const void *bias, void *y,
+                    int64_t M, int64_t N, int64_t K,
+                    float eps, int norm, int act, int dtype, void *stream);
+
+/*
+ * Fused FFN (page "昇腾CANN的MatMul融合玩法，让大模型推理快3倍", section 二,
+ * strategy 2: FFN(x) = MatMul2(SiLU(MatMul1(x)))), with an optional
+ * normalization prologue and optional biases:
+ *
+ *     h[M,F] = act( norm_affine(x)[M,K] . W1[F,K]^T + b1[F] )   (stored as dtype)
+ *     y[M,N] = h . W2[N,F]^T + b2[N]
+ *
+ * h lives in the caller-provided workspace (device memory of at least
+ * fused_ffn_workspace_size(M, F, dtype) bytes, 256-byte aligned recommended).
+ * Two kernel launches on `stream`, in order. The workspace must not overlap
+ * any input or y; it may be reused once the call's work has completed on the
+ * stream. Returns an ng_status_t.
+ */
+size_t fused_ffn_workspace_size(int64_t M, int64_t F, int dtype);
+
+int fused_ffn(const void *x, const void *gamma, const void *beta,
+              const void *W1, const void *b1, const void *W2, const void *b2,
+              void *y, int64_t M, int64_t K, int64_t F, int64_t N,
+              float eps, int norm, int act, int dtype,
+              void *workspace, size_t workspace_bytes, void *stream);
+
+/* Human-readable text of a status code (static storage, never NULL). */
+const char *norm_gemm_status_string(int status);
+
+/* NORM_GEMM_ABI_VERSION of the loaded library. */
+int norm_gemm_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NORM_GEMM_H */

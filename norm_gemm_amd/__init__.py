@@ -1,0 +1,192 @@
+"""Python binding of ``libnormgemm.so``: argument marshalling only.
+
+Every step of the computation runs in the library's HIP kernels; PyTorch
+supplies device memory and the stream. The functions mirror the C ABI in
+``include/norm_gemm.h`` and keep its names:
+
+* :func:`fused_norm_gemm` -- y = act(norm_affine(x) @ W.T + bias)
+* :func:`fused_ffn` -- y = act(norm_affine(x) @ W1.T + b1) @ W2.T + b2
+* :func:`fused_ffn_workspace_size`, :func:`norm_gemm_status_string`,
+  :func:`norm_gemm_abi_version`
+
+There is no fallback: importing this package without the built library
+raises ImportError, and a failing status raises :class:`NormGemmError`.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+# torch first: it loads the HIP runtime that the library then shares (same
+# soname), so streams and device pointers from torch are valid in the library.
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY_PATH = os.path.join(_HERE, "libnormgemm.so")
+
+NORMS = {"none": 0, "layernorm": 1, "rmsnorm": 2}
+ACTS = {"none": 0, "silu": 1}
+DTYPES = {torch.float16: 0, torch.bfloat16: 1}
+
+# Symbols declared in include/norm_gemm.h.
+EXPORTED = ("fused_norm_gemm", "fused_ffn", "fused_ffn_workspace_size",
+            "norm_gemm_status_string", "norm_gemm_abi_version")
+
+
+class NormGemmError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {norm_gemm_status_string(status)} (status {status})")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIBRARY_PATH):
+        raise ImportError(f"{LIBRARY_PATH} is not built; run `python -m norm_gemm_amd.build`")
+    L = ctypes.CDLL(LIBRARY_PATH)
+    vp, i64, f32, ci, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int, ctypes.c_size_t
+    L.fused_norm_gemm.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, f32, ci, ci, ci, vp]
+    L.fused_norm_gemm.restype = ci
+    L.fused_ffn_workspace_size.argtypes = [i64, i64, ci]
+    L.fused_ffn_workspace_size.restype = sz
+    L.fused_ffn.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, f32, ci, ci,
+                            ci, vp, sz, vp]
+    L.fused_ffn.restype = ci
+    L.norm_gemm_status_string.argtypes = [ci]
+    L.norm_gemm_status_string.restype = ctypes.c_char_p
+    L.norm_gemm_abi_version.argtypes = []
+    L.norm_gemm_abi_version.restype = ci
+    return L
+
+
+lib = _load()
+
+
+def norm_gemm_status_string(status: int) -> str:
+    return lib.norm_gemm_status_string(int(status)).decode()
+
+
+def norm_gemm_abi_version() -> int:
+    return int(lib.norm_gemm_abi_version())
+
+
+def fused_ffn_workspace_size(M: int, F: int, dtype) -> int:
+    d = DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(lib.fused_ffn_workspace_size(int(M), int(F), d))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _check(t: Optional[torch.Tensor], name: str, dtype, device, shape=None):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda" or t.device != device:
+        raise ValueError(f"{name} must live on {device}, got {t.device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _enum(table, value, name):
+    if isinstance(value, str):
+        if value not in table:
+            raise ValueError(f"unknown {name} {value!r}; choose from {sorted(table)}")
+        return table[value]
+    return int(value)
+
+
+def _stream(device, stream):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def fused_norm_gemm(x: torch.Tensor, weight: torch.Tensor, gamma: Optional[torch.Tensor] = None,
+                    beta: Optional[torch.Tensor] = None, bias: Optional[torch.Tensor] = None, *,
+                    eps: float = 1e-5, norm="layernorm", act="none",
+                    out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """y[..., N] = act(norm_affine(x)[..., K] @ weight[N, K].T + bias[N]).
+
+    ``x`` may have leading dimensions (e.g. [batch, seq, hidden]); they are
+    flattened into M. Returns ``out`` (allocated when not given).
+    """
+    if not isinstance(x, torch.Tensor) or x.dim() < 1:
+        raise ValueError("x must be a tensor with at least one dimension")
+    if x.dtype not in DTYPES:
+        raise ValueError(f"x must be float16 or bfloat16, got {x.dtype}")
+    dev = x.device
+    K = x.shape[-1]
+    M = x.numel() // K if K else 0
+    if weight is None or weight.dim() != 2 or weight.shape[1] != K:
+        raise ValueError(f"weight must be [N, {K}]")
+    N = weight.shape[0]
+    _check(x, "x", x.dtype, dev)
+    _check(weight, "weight", x.dtype, dev)
+    _check(gamma, "gamma", x.dtype, dev, (K,))
+    _check(beta, "beta", x.dtype, dev, (K,))
+    _check(bias, "bias", x.dtype, dev, (N,))
+    lead = tuple(x.shape[:-1])
+    if out is None:
+        out = torch.empty(lead + (N,), dtype=x.dtype, device=dev)
+    _check(out, "out", x.dtype, dev, lead + (N,))
+    with torch.cuda.device(dev):
+        st = lib.fused_norm_gemm(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(weight), _ptr(bias),
+                                 _ptr(out), M, N, K, float(eps), _enum(NORMS, norm, "norm"),
+                                 _enum(ACTS, act, "act"), DTYPES[x.dtype], _stream(dev, stream))
+    if st != 0:
+        raise NormGemmError(st, "fused_norm_gemm")
+    return out
+
+
+def fused_ffn(x: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor,
+              gamma: Optional[torch.Tensor] = None, beta: Optional[torch.Tensor] = None,
+              b1: Optional[torch.Tensor] = None, b2: Optional[torch.Tensor] = None, *,
+              eps: float = 1e-5, norm="none", act="silu",
+              workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+              stream=None) -> torch.Tensor:
+    """y = act(norm_affine(x) @ w1[F, K].T + b1) @ w2[N, F].T + b2.
+
+    The intermediate h[M, F] lives in ``workspace`` (a uint8 device tensor of
+    at least :func:`fused_ffn_workspace_size` bytes; allocated when not given).
+    """
+    if not isinstance(x, torch.Tensor) or x.dim() < 1:
+        raise ValueError("x must be a tensor with at least one dimension")
+    if x.dtype not in DTYPES:
+        raise ValueError(f"x must be float16 or bfloat16, got {x.dtype}")
+    dev = x.device
+    K = x.shape[-1]
+    M = x.numel() // K if K else 0
+    if w1 is None or w1.dim() != 2 or w1.shape[1] != K:
+        raise ValueError(f"w1 must be [F, {K}]")
+    F = w1.shape[0]
+    if w2 is None or w2.dim() != 2 or w2.shape[1] != F:
+        raise ValueError(f"w2 must be [N, {F}]")
+    N = w2.shape[0]
+    for t, name, shp in ((x, "x", None), (w1, "w1", None), (w2, "w2", None), (gamma, "gamma", (K,)),
+                         (beta, "beta", (K,)), (b1, "b1", (F,)), (b2, "b2", (N,))):
+        _check(t, name, x.dtype, dev, shp)
+    need = fused_ffn_workspace_size(M, F, x.dtype)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on x's device")
+    lead = tuple(x.shape[:-1])
+    if out is None:
+        out = torch.empty(lead + (N,), dtype=x.dtype, device=dev)
+    _check(out, "out", x.dtype, dev, lead + (N,))
+    ws_bytes = workspace.numel() * workspace.element_size()
+    with torch.cuda.device(dev):
+        st = lib.fused_ffn(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(w1), _ptr(b1), _ptr(w2),
+                           _ptr(b2), _ptr(out), M, K, F, N, float(eps),
+                           _enum(NORMS, norm, "norm"), _enum(ACTS, act, "act"),
+                           DTYPES[x.dtype], _ptr(workspace), ws_bytes, _stream(dev, stream))
+    if st != 0:
+        raise NormGemmError(st, "fused_ffn")
+    return out

@@ -1,0 +1,101 @@
+// api.cpp -- the extern "C" entry points declared in include/norm_gemm.h:
+// validate (pure host code), pick the kernel, launch on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include "launch.h"
+#include "norm_gemm.h"
+#include "validate.h"
+
+namespace {
+
+ng::GemmArgs make_args(const void *x, const void *gamma, const void *beta, const void *W,
+                       const void *bias, void *y, int64_t M, int64_t N, int64_t K, float eps,
+                       int norm, int act, int dtype)
+{
+    ng::GemmArgs a;
+    a.x = x;
+    a.gamma = norm == NG_NORM_NONE ? nullptr : gamma;
+    a.beta = norm == NG_NORM_NONE ? nullptr : beta;
+    a.W = W;
+    a.bias = bias;
+    a.y = y;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.eps = eps;
+    a.norm = norm;
+    a.act = act;
+    a.dtype = dtype;
+    a.vec = ng_vector_ok(K, x, W, a.gamma, a.beta) != 0;
+    return a;
+}
+
+int run(const ng::GemmArgs &a, hipStream_t s)
+{
+    hipError_t e = (a.M <= ng::kDecodeMaxM) ? ng::launch_decode(a, s) : ng::launch_prefill(a, s);
+    return e == hipSuccess ? NG_OK : NG_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fused_norm_gemm(const void *x, const void *gamma, const void *beta, const void *W,
+                    const void *bias, void *y, int64_t M, int64_t N, int64_t K, float eps,
+                    int norm, int act, int dtype, void *stream)
+{
+    int st = ng_validate_gemm(x, gamma, beta, W, bias, y, M, N, K, eps, norm, act, dtype);
+    if (st != NG_OK)
+        return st;
+    return run(make_args(x, gamma, beta, W, bias, y, M, N, K, eps, norm, act, dtype),
+               (hipStream_t)stream);
+}
+
+size_t fused_ffn_workspace_size(int64_t M, int64_t F, int dtype)
+{
+    return ng_ffn_workspace_size(M, F, dtype);
+}
+
+int fused_ffn(const void *x, const void *gamma, const void *beta, const void *W1,
+              const void *b1, const void *W2, const void *b2, void *y, int64_t M, int64_t K,
+              int64_t F, int64_t N, float eps, int norm, int act, int dtype, void *workspace,
+              size_t workspace_bytes, void *stream)
+{
+    int st = ng_validate_ffn(x, gamma, beta, W1, b1, W2, b2, y, M, K, F, N, eps, norm, act,
+                             dtype, workspace, workspace_bytes);
+    if (st != NG_OK)
+        return st;
+    hipStream_t s = (hipStream_t)stream;
+    // phase 1: h = act(norm_affine(x) . W1^T + b1), kept in the workspace
+    st = run(make_args(x, gamma, beta, W1, b1, workspace, M, F, K, eps, norm, act, dtype), s);
+    if (st != NG_OK)
+        return st;
+    // phase 2: y = h . W2^T + b2
+    return run(make_args(workspace, nullptr, nullptr, W2, b2, y, M, N, F, 0.0f, NG_NORM_NONE,
+                         NG_ACT_NONE, dtype),
+               s);
+}
+
+const char *norm_gemm_status_string(int status)
+{
+    switch (status) {
+    case NG_OK: return "ok";
+    case NG_ERR_NULL: return "a required pointer is NULL";
+    case NG_ERR_SHAPE: return "invalid shape (M, N, K and F must be in [1, 2^31-1])";
+    case NG_ERR_ENUM: return "norm, act or dtype out of range";
+    case NG_ERR_EPS: return "eps must be finite and >= 0";
+    case NG_ERR_ALIAS: return "the output overlaps an input or the workspace";
+    case NG_ERR_WORKSPACE: return "workspace missing or too small";
+    case NG_ERR_UNSUPPORTED: return "unsupported request";
+    case NG_ERR_ALIGN: return "a pointer is not 2-byte aligned";
+    case NG_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+int norm_gemm_abi_version(void)
+{
+    return NORM_GEMM_ABI_VERSION;
+}
+
+}  // extern "C"

@@ -1,0 +1,187 @@
+// device_common.h -- gfx950 device helpers shared by the prefill and decode
+// kernels: 16-bit storage formats, 128-bit chunk conversion, wave reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ng {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+enum { DT_F16 = 0, DT_BF16 = 1 };
+
+// ---------------------------------------------------------------- scalars
+template <int DT> __device__ __forceinline__ float lo_to_f(uint32_t w);
+template <int DT> __device__ __forceinline__ float hi_to_f(uint32_t w);
+
+template <> __device__ __forceinline__ float lo_to_f<DT_F16>(uint32_t w)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+}
+template <> __device__ __forceinline__ float hi_to_f<DT_F16>(uint32_t w)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+// bf16 is the upper half of a binary32: widening is a shift.
+template <> __device__ __forceinline__ float lo_to_f<DT_BF16>(uint32_t w)
+{
+    return __builtin_bit_cast(float, w << 16);
+}
+template <> __device__ __forceinline__ float hi_to_f<DT_BF16>(uint32_t w)
+{
+    return __builtin_bit_cast(float, w & 0xffff0000u);
+}
+
+template <int DT> __device__ __forceinline__ float bits_to_f(uint16_t b)
+{
+    return lo_to_f<DT>((uint32_t)b);
+}
+
+// Round two floats to the storage type (round-to-nearest-even) and pack
+// them into one dword, low half first.
+template <int DT> __device__ __forceinline__ uint32_t pack2(float a, float b);
+
+template <> __device__ __forceinline__ uint32_t pack2<DT_F16>(float a, float b)
+{
+    uint32_t lo = __builtin_bit_cast(uint16_t, (_Float16)a);
+    uint32_t hi = __builtin_bit_cast(uint16_t, (_Float16)b);
+    return lo | (hi << 16);
+}
+template <> __device__ __forceinline__ uint32_t pack2<DT_BF16>(float a, float b)
+{
+    uint32_t lo = __builtin_bit_cast(uint16_t, (__bf16)a);
+    uint32_t hi = __builtin_bit_cast(uint16_t, (__bf16)b);
+    return lo | (hi << 16);
+}
+
+template <int DT> __device__ __forceinline__ uint16_t f_to_bits(float a)
+{
+    return (uint16_t)(pack2<DT>(a, 0.0f) & 0xffffu);
+}
+
+// ------------------------------------------------------- 128-bit chunks
+// A chunk is 8 consecutive elements (16 bytes) of one row.
+template <int DT> __device__ __forceinline__ void unpack8(const u32x4 &c, float *f)
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = lo_to_f<DT>(c[i]);
+        f[2 * i + 1] = hi_to_f<DT>(c[i]);
+    }
+}
+
+template <int DT> __device__ __forceinline__ u32x4 pack8(const float *f)
+{
+    u32x4 c;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        c[i] = pack2<DT>(f[2 * i], f[2 * i + 1]);
+    return c;
+}
+
+__device__ __forceinline__ u32x4 ldg128(const uint16_t *p)
+{
+    return *reinterpret_cast<const u32x4 *>(p);
+}
+
+// Element-wise chunk load with bounds: elements k0..k0+7 of a row of length
+// `len`; positions at or beyond `len` read as +0.
+__device__ __forceinline__ u32x4 ldg_elems(const uint16_t *row, int64_t k0, int64_t len)
+{
+    uint16_t e[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        e[i] = (k0 + i < len) ? row[k0 + i] : (uint16_t)0;
+    u32x4 c;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        c[i] = (uint32_t)e[2 * i] | ((uint32_t)e[2 * i + 1] << 16);
+    return c;
+}
+
+// Chunk of 8 elements starting at k0 of a row of length `len`:
+// VEC (len % 8 == 0, 16-byte aligned) -> one 128-bit load or zeros.
+template <bool VEC>
+__device__ __forceinline__ u32x4 load_chunk(const uint16_t *row, int64_t k0, int64_t len)
+{
+    if constexpr (VEC) {
+        if (k0 < len)
+            return ldg128(row + k0);
+        return u32x4{0u, 0u, 0u, 0u};
+    } else {
+        return ldg_elems(row, k0, len);
+    }
+}
+
+// ---------------------------------------------------------- reductions
+__device__ __forceinline__ float wave_sum(float v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// ----------------------------------------------------------- epilogue
+enum { ACT_NONE = 0, ACT_SILU = 1 };
+
+// SiLU(z) = z * sigmoid(z) = z / (1 + e^-z); exp from the device library.
+__device__ __forceinline__ float apply_act(float z, int act)
+{
+    if (act == ACT_SILU)
+        return z / (1.0f + __expf(-z));
+    return z;
+}
+
+// Row statistics -> (rs, mu) such that the normalized value is
+// (x - mu) * rs: LayerNorm mu = mean, rs = 1/sqrt(var+eps);
+// RMSNorm mu = 0, rs = 1/sqrt(mean(x^2)+eps). Subtracting the mean before
+// scaling keeps x == mean exactly zero (a constant row normalizes to 0).
+enum { NORM_NONE = 0, NORM_LAYERNORM = 1, NORM_RMSNORM = 2 };
+
+// One-pass statistics of a row with the shifted-data algorithm (Chan, Golub
+// and LeVeque, "Algorithms for computing the sample variance", 1983): sums of
+// d = x - x[0] and d^2 in fp32, so that a large common offset does not cancel
+// in var = E[d^2] - E[d]^2.  One wave per row; VEC uses 128-bit loads.
+template <int DT, bool VEC>
+__device__ __forceinline__ void row_stats(const uint16_t *row, int64_t K, float eps,
+                                          int norm, int lane, float &rs, float &mu)
+{
+    const float shift = (norm == NORM_LAYERNORM) ? bits_to_f<DT>(row[0]) : 0.0f;
+    float s1 = 0.0f, s2 = 0.0f;
+    const int64_t nchunk = (K + 7) / 8;
+    for (int64_t c = lane; c < nchunk; c += 64) {
+        u32x4 raw = load_chunk<VEC>(row, c * 8, K);
+        float f[8];
+        unpack8<DT>(raw, f);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            // padded positions (k >= K) read as 0 and must not contribute
+            float d = (c * 8 + i < K) ? f[i] - shift : 0.0f;
+            s1 += d;
+            s2 = fmaf(d, d, s2);
+        }
+    }
+    s1 = wave_sum(s1);
+    s2 = wave_sum(s2);
+    const float invK = 1.0f / (float)K;
+    if (norm == NORM_LAYERNORM) {
+        float md = s1 * invK;
+        float var = fmaxf(fmaf(-md, md, s2 * invK), 0.0f);
+        rs = rsqrtf(var + eps);
+        mu = shift + md;
+    } else if (norm == NORM_RMSNORM) {
+        rs = rsqrtf(s2 * invK + eps);
+        mu = 0.0f;
+    } else {
+        rs = 1.0f;
+        mu = 0.0f;
+    }
+}
+
+}  // namespace ng

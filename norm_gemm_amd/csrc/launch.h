@@ -1,0 +1,24 @@
+// launch.h -- host-side launch descriptor shared by the C ABI and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ng {
+
+// One validated GEMM request; pointers are device addresses.
+struct GemmArgs {
+    const void *x, *gamma, *beta, *W, *bias;
+    void *y;
+    int64_t M, N, K;
+    float eps;
+    int norm, act, dtype;
+    bool vec;  // K % 8 == 0 and x, W, gamma, beta 16-byte aligned
+};
+
+hipError_t launch_prefill(const GemmArgs &a, hipStream_t s);
+hipError_t launch_decode(const GemmArgs &a, hipStream_t s);
+
+constexpr int64_t kDecodeMaxM = 32;
+
+}  // namespace ng

@@ -1,0 +1,132 @@
+/* validate.c -- argument checks of the C ABI (pure host code, no HIP). */
+#include "validate.h"
+
+#include <math.h>
+
+#include "norm_gemm.h"
+
+/* Kernels index rows and columns with 32-bit ints and offsets with 64 bits. */
+#define NG_MAX_DIM ((int64_t)0x7fffffff)
+
+typedef struct {
+    uintptr_t lo, hi; /* [lo, hi) */
+} range_t;
+
+static range_t rng(const void *p, int64_t elems)
+{
+    range_t r;
+    r.lo = (uintptr_t)p;
+    r.hi = p ? r.lo + (uintptr_t)elems * 2u : r.lo;
+    return r;
+}
+
+static int overlap(range_t a, range_t b)
+{
+    if (a.lo == a.hi || b.lo == b.hi)
+        return 0;
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+static int mul_ok(int64_t a, int64_t b)
+{
+    return a <= (INT64_MAX / 4) / b; /* keeps byte counts of a*b elements in range */
+}
+
+static int enums_ok(int norm, int act, int dtype)
+{
+    return norm >= NG_NORM_NONE && norm <= NG_NORM_RMSNORM && act >= NG_ACT_NONE &&
+           act <= NG_ACT_SILU && (dtype == NG_DTYPE_F16 || dtype == NG_DTYPE_BF16);
+}
+
+static int dim_ok(int64_t d)
+{
+    return d >= 1 && d <= NG_MAX_DIM;
+}
+
+static int eps_ok(float eps, int norm)
+{
+    if (norm == NG_NORM_NONE)
+        return 1;
+    return isfinite(eps) && eps >= 0.0f;
+}
+
+static int align2(const void *p)
+{
+    return ((uintptr_t)p & 1u) == 0;
+}
+
+int ng_validate_gemm(const void *x, const void *gamma, const void *beta, const void *W,
+                     const void *bias, const void *y, int64_t M, int64_t N, int64_t K,
+                     float eps, int norm, int act, int dtype)
+{
+    if (!x || !W || !y)
+        return NG_ERR_NULL;
+    if (!enums_ok(norm, act, dtype))
+        return NG_ERR_ENUM;
+    if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K) || !mul_ok(M, K) || !mul_ok(N, K) ||
+        !mul_ok(M, N))
+        return NG_ERR_SHAPE;
+    if (!eps_ok(eps, norm))
+        return NG_ERR_EPS;
+    if (!align2(x) || !align2(gamma) || !align2(beta) || !align2(W) || !align2(bias) ||
+        !align2(y))
+        return NG_ERR_ALIGN;
+    range_t ry = rng(y, M * N);
+    if (overlap(ry, rng(x, M * K)) || overlap(ry, rng(W, N * K)) ||
+        overlap(ry, rng(gamma, K)) || overlap(ry, rng(beta, K)) || overlap(ry, rng(bias, N)))
+        return NG_ERR_ALIAS;
+    return NG_OK;
+}
+
+size_t ng_ffn_workspace_size(int64_t M, int64_t F, int dtype)
+{
+    if (M < 1 || F < 1 || (dtype != NG_DTYPE_F16 && dtype != NG_DTYPE_BF16) || !mul_ok(M, F))
+        return 0;
+    size_t bytes = (size_t)M * (size_t)F * 2u;
+    return (bytes + 255u) & ~(size_t)255u;
+}
+
+int ng_validate_ffn(const void *x, const void *gamma, const void *beta, const void *W1,
+                    const void *b1, const void *W2, const void *b2, const void *y,
+                    int64_t M, int64_t K, int64_t F, int64_t N, float eps, int norm, int act,
+                    int dtype, const void *workspace, size_t workspace_bytes)
+{
+    if (!x || !W1 || !W2 || !y)
+        return NG_ERR_NULL;
+    if (!enums_ok(norm, act, dtype))
+        return NG_ERR_ENUM;
+    if (!dim_ok(M) || !dim_ok(K) || !dim_ok(F) || !dim_ok(N) || !mul_ok(M, K) ||
+        !mul_ok(F, K) || !mul_ok(N, F) || !mul_ok(M, F) || !mul_ok(M, N))
+        return NG_ERR_SHAPE;
+    if (!eps_ok(eps, norm))
+        return NG_ERR_EPS;
+    if (!align2(x) || !align2(gamma) || !align2(beta) || !align2(W1) || !align2(b1) ||
+        !align2(W2) || !align2(b2) || !align2(y) || !align2(workspace))
+        return NG_ERR_ALIGN;
+    range_t in[7] = {rng(x, M * K), rng(gamma, K), rng(beta, K), rng(W1, F * K),
+                     rng(b1, F),    rng(W2, N * F), rng(b2, N)};
+    range_t ry = rng(y, M * N);
+    for (int i = 0; i < 7; ++i)
+        if (overlap(ry, in[i]))
+            return NG_ERR_ALIAS;
+    if (!workspace || workspace_bytes < ng_ffn_workspace_size(M, F, dtype))
+        return NG_ERR_WORKSPACE;
+    range_t rw = rng(workspace, M * F);
+    if (overlap(rw, ry))
+        return NG_ERR_ALIAS;
+    for (int i = 0; i < 7; ++i)
+        if (overlap(rw, in[i]))
+            return NG_ERR_ALIAS;
+    return NG_OK;
+}
+
+int ng_vector_ok(int64_t K, const void *a, const void *b, const void *c, const void *d)
+{
+    const void *p[4] = {a, b, c, d};
+    if (K % 8 != 0)
+        return 0;
+    for (int i = 0; i < 4; ++i)
+        if (p[i] && ((uintptr_t)p[i] & 15u) != 0)
+            return 0;
+    return 1;
+}

@@ -1,0 +1,33 @@
+/* validate.h -- argument checks of the C ABI; pure host code, no HIP calls. */
+#ifndef NG_VALIDATE_H
+#define NG_VALIDATE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Returns NG_OK or the first failing ng_status_t, checked in this order:
+ * NULL pointers, enums, shapes, eps, 2-byte alignment, output aliasing. */
+int ng_validate_gemm(const void *x, const void *gamma, const void *beta, const void *W,
+                     const void *bias, const void *y, int64_t M, int64_t N, int64_t K,
+                     float eps, int norm, int act, int dtype);
+
+/* As above for the FFN; adds the workspace (size and aliasing) last. */
+int ng_validate_ffn(const void *x, const void *gamma, const void *beta, const void *W1,
+                    const void *b1, const void *W2, const void *b2, const void *y,
+                    int64_t M, int64_t K, int64_t F, int64_t N, float eps, int norm, int act,
+                    int dtype, const void *workspace, size_t workspace_bytes);
+
+/* 1 when every given pointer is 16-byte aligned and K % 8 == 0. */
+int ng_vector_ok(int64_t K, const void *a, const void *b, const void *c, const void *d);
+
+size_t ng_ffn_workspace_size(int64_t M, int64_t F, int dtype);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif

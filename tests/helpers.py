@@ -1,0 +1,62 @@
+"""Shared helpers of the GPU tests: upload seeded inputs, call the library,
+compare with the oracle under the acceptance metric."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import synth
+
+TOL = 1e-2  # max |gpu - ref| / (|ref| + 1), fp16/bf16 output, fp32 accumulation
+
+
+def tdtype(dtype: int):
+    return torch.float16 if dtype == synth.F16 else torch.bfloat16
+
+
+def upload(bits, dtype: int, device="cuda"):
+    if bits is None:
+        return None
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(tdtype(dtype)).to(device)
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def rel_err(gpu: np.ndarray, ref: np.ndarray) -> float:
+    assert gpu.shape == ref.shape
+    if gpu.size == 0:
+        return 0.0
+    return float(np.max(np.abs(gpu - ref) / (np.abs(ref) + 1.0)))
+
+
+def assert_close(gpu: np.ndarray, ref: np.ndarray, tol: float = TOL, what: str = ""):
+    fin = np.isfinite(ref)
+    assert np.all(np.isfinite(gpu[fin])), f"{what}: non-finite GPU value where ref is finite"
+    err = rel_err(gpu[fin], ref[fin])
+    assert err <= tol, f"{what}: max |gpu-ref|/(|ref|+1) = {err:.3e} > {tol}"
+    return err
+
+
+def run_case_gpu(case, device="cuda"):
+    """Run a synth.Case through the library; returns the output tensor."""
+    import norm_gemm_amd as ng
+    A = case.arrays
+    up = lambda k: upload(A.get(k), case.dtype, device)
+    norm = case.norm
+    act = case.act
+    if case.kind == "ffn":
+        return ng.fused_ffn(up("x"), up("W1"), up("W2"), up("gamma"), up("beta"), up("b1"),
+                            up("b2"), eps=case.eps, norm=norm, act=act)
+    return ng.fused_norm_gemm(up("x"), up("W"), up("gamma"), up("beta"), up("bias"),
+                              eps=case.eps, norm=norm, act=act)
+
+
+def sample_indices(n: int, extra: int, seed: int, tile: int = 128):
+    """Edges of the first, second and last tiles plus random interior indices."""
+    base = {0, 1, n - 1, n - 2, min(n - 1, tile - 1), min(n - 1, tile), n // 2}
+    rng = np.random.default_rng(seed)
+    base |= set(int(v) for v in rng.integers(0, n, size=extra))
+    return sorted(i for i in base if 0 <= i < n)

@@ -1,0 +1,271 @@
+"""GPU parity: the HIP path against the fp64 oracle on the same seeded inputs.
+
+Acceptance: max |gpu - ref| / (|ref| + 1) <= 1e-2 (fp16/bf16 output, fp32
+accumulation), every GPU value finite where the oracle's is; integer GEMMs
+must match bit for bit. Small shapes compare every output and span several
+tiles with ragged tails; the full-size workloads compare sampled rows and
+columns (edges of the first and last tiles plus random interior ones) in the
+same launch configuration the benchmark times.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from helpers import TOL, assert_close, run_case_gpu, sample_indices, to_f64, upload
+
+pytestmark = pytest.mark.gpu
+
+LN, RMS, NONE = synth.NORM_LAYERNORM, synth.NORM_RMSNORM, synth.NORM_NONE
+SILU, ACT0 = synth.ACT_SILU, synth.ACT_NONE
+F16, BF16 = synth.F16, synth.BF16
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import norm_gemm_amd  # noqa: F401  (fails loudly when the library is missing)
+    yield
+    torch.cuda.synchronize()
+
+
+def check_full(case, tol=TOL):
+    y = run_case_gpu(case)
+    torch.cuda.synchronize()
+    ref = oracle.run_case(case)
+    err = assert_close(to_f64(y).reshape(ref.shape), ref, tol, case.name)
+    print(f"{case.name}: max rel err {err:.3e}", flush=True)
+    return y, ref
+
+
+# ---------------------------------------------------------------- small shapes
+def test_ln_linear_bias_64x256_every_output():
+    check_full(synth.ln_linear_bias_64x256())
+
+
+PREFILL_SHAPES = [(33, 17, 13), (65, 129, 257), (129, 65, 64), (200, 300, 1001),
+                  (257, 513, 520), (96, 256, 8), (300, 40, 7)]
+
+
+@pytest.mark.parametrize("M,N,K", PREFILL_SHAPES)
+@pytest.mark.parametrize("norm,act,dtype", [(LN, ACT0, F16), (RMS, SILU, F16), (NONE, SILU, BF16),
+                                            (LN, SILU, BF16)])
+def test_prefill_ragged_shapes(M, N, K, norm, act, dtype):
+    case = synth.make_norm_gemm(f"prefill_{M}x{N}x{K}_n{norm}a{act}d{dtype}", M, K, N,
+                                dtype=dtype, norm=norm, act=act, eps=1e-5, seed=M + N + K)
+    check_full(case)
+
+
+DECODE_SHAPES = [(1, 16, 8), (1, 300, 1000), (3, 100, 37), (8, 129, 256), (16, 64, 520),
+                 (17, 300, 264), (31, 48, 1001), (32, 1000, 2048)]
+
+
+@pytest.mark.parametrize("M,N,K", DECODE_SHAPES)
+@pytest.mark.parametrize("norm,act,dtype", [(RMS, ACT0, BF16), (LN, SILU, F16), (NONE, ACT0, F16)])
+def test_decode_ragged_shapes(M, N, K, norm, act, dtype):
+    case = synth.make_norm_gemm(f"decode_{M}x{N}x{K}_n{norm}a{act}d{dtype}", M, K, N,
+                                dtype=dtype, norm=norm, act=act, eps=1e-6, seed=M * 7 + N + K)
+    check_full(case)
+
+
+@pytest.mark.parametrize("M", [5, 100])
+@pytest.mark.parametrize("gamma,beta,bias", [(False, False, False), (True, False, True),
+                                             (False, True, False)])
+def test_optional_gamma_beta_bias(M, gamma, beta, bias):
+    case = synth.make_norm_gemm(f"opt_{M}_{gamma}{beta}{bias}", M, 136, 72, norm=LN, act=SILU,
+                                gamma=gamma, beta=beta, bias=bias, seed=3)
+    check_full(case)
+
+
+@pytest.mark.parametrize("M", [7, 130])
+def test_rmsnorm_with_beta(M):
+    case = synth.make_norm_gemm(f"rms_beta_{M}", M, 96, 80, norm=RMS, act=ACT0, seed=4)
+    check_full(case)
+
+
+@pytest.mark.parametrize("M,K", [(9, 64), (140, 264)])
+def test_unaligned_pointers_take_element_loads(M, K):
+    """Pointers that are 2- but not 16-byte aligned must still be exact."""
+    case = synth.make_norm_gemm(f"unaligned_{M}x{K}", M, K, 50, norm=LN, act=SILU, seed=5)
+    import norm_gemm_amd as ng
+    A = case.arrays
+
+    def shifted(bits):
+        t = upload(bits, case.dtype)
+        buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+        v = buf[1:].view(t.shape)
+        v.copy_(t)
+        return v
+
+    y = ng.fused_norm_gemm(shifted(A["x"]), shifted(A["W"]), shifted(A["gamma"]),
+                           shifted(A["beta"]), shifted(A["bias"]), eps=case.eps, norm=LN, act=SILU)
+    torch.cuda.synchronize()
+    assert_close(to_f64(y), oracle.run_case(case), what=case.name)
+
+
+def test_stress_large_mean_layernorm():
+    """x ~ N(4, 1): the one-pass fp32 variance must not cancel."""
+    for M in (20, 150):
+        case = synth.make_norm_gemm(f"shifted_mean_{M}", M, 4096, 96, norm=LN, act=ACT0,
+                                    x_mean=4.0, seed=6)
+        check_full(case)
+
+
+# --------------------------------------------------------- closed forms / exact
+@pytest.mark.parametrize("M,dtype", [(12, F16), (77, F16), (20, BF16), (200, BF16)])
+def test_identity_weight_returns_normalized_rows(M, dtype):
+    import norm_gemm_amd as ng
+    K = 256
+    case = synth.make_norm_gemm(f"identity_{M}", M, K, K, dtype=dtype, norm=LN, seed=7,
+                                bias=False)
+    eye = np.eye(K, dtype=np.float32)
+    case.arrays["W"] = synth.bits_from_f32(eye, dtype)
+    check_full(case)
+    # The products are exact and each sum has one nonzero term, so y is the
+    # kernel's own normalized operand: gamma/beta = (1, 0) gives x_hat itself.
+    A = case.arrays
+    y = ng.fused_norm_gemm(upload(A["x"], dtype), upload(A["W"], dtype), eps=case.eps, norm=LN)
+    torch.cuda.synchronize()
+    ref = oracle.normalize(A["x"], None, None, case.eps, LN, dtype)
+    assert_close(to_f64(y), ref, what="identity, no affine")
+
+
+@pytest.mark.parametrize("M", [6, 96])
+def test_constant_rows_give_act_of_beta_w_plus_bias(M):
+    K, N = 512, 64
+    case = synth.make_norm_gemm(f"constant_{M}", M, K, N, norm=LN, act=SILU, seed=8)
+    c = np.linspace(-3.0, 3.0, M, dtype=np.float32)[:, None] * np.ones((1, K), np.float32)
+    case.arrays["x"] = synth.f32_to_f16_bits(c)
+    y, ref = check_full(case)
+    yb = to_f64(y)
+    # The one-pass statistics shift by the row's first element, so the mean of
+    # a constant row is exact, x - mean == 0 and a == beta: every row of y has
+    # the same bit pattern.
+    for m in range(1, M):
+        assert np.array_equal(yb[m], yb[0])
+
+
+@pytest.mark.parametrize("M,dtype,K", [(40, F16, 128), (3, F16, 128), (70, BF16, 64), (5, BF16, 64)])
+def test_integer_gemm_is_bit_exact(M, dtype, K):
+    """norm NONE with integer x and W in [-2, 2]: products and fp32 sums are
+    exact and |y| stays within the integers the output type holds exactly."""
+    import norm_gemm_amd as ng
+    rng = np.random.default_rng(M + K)
+    N = 96
+    x = rng.integers(-2, 3, (M, K)).astype(np.float32)
+    W = rng.integers(-2, 3, (N, K)).astype(np.float32)
+    bias = rng.integers(-3, 4, N).astype(np.float32)
+    xb, Wb, bb = (synth.bits_from_f32(v, dtype) for v in (x, W, bias))
+    y = ng.fused_norm_gemm(upload(xb, dtype), upload(Wb, dtype), bias=upload(bb, dtype), norm=NONE)
+    torch.cuda.synchronize()
+    ref = oracle.norm_gemm(xb, None, None, Wb, bb, 1e-5, NONE, ACT0, dtype)
+    assert np.array_equal(to_f64(y), ref)
+
+
+@pytest.mark.parametrize("M", [4, 64])
+def test_silu_closed_form_and_zero(M):
+    import norm_gemm_amd as ng
+    K, N = 64, 81
+    bias = synth.f32_to_f16_bits(np.linspace(-20, 20, N, dtype=np.float32))
+    x = synth.normal_bits(np.random.default_rng(9), (M, K), 0.0, 1.0, F16)
+    W0 = np.zeros((N, K), np.uint16)
+    y = ng.fused_norm_gemm(upload(x, F16), upload(W0, F16), bias=upload(bias, F16), norm=LN,
+                           act="silu")
+    y0 = ng.fused_norm_gemm(upload(x, F16), upload(W0, F16), norm=LN, act="silu")
+    torch.cuda.synchronize()
+    ref = oracle.norm_gemm(x, None, None, W0, bias, 1e-5, LN, SILU, F16)
+    assert_close(to_f64(y), ref, what="silu(bias)")
+    z = to_f64(y0)
+    assert np.all(z == 0.0) and not np.any(np.signbit(z))
+
+
+# ------------------------------------------------------------- run properties
+@pytest.mark.parametrize("M", [8, 200])
+def test_deterministic_and_guard_bands_untouched(M):
+    import norm_gemm_amd as ng
+    case = synth.make_norm_gemm(f"det_{M}", M, 1024, 384, norm=RMS, act=SILU, seed=10)
+    A = case.arrays
+    args = [upload(A[k], F16) for k in ("x", "W", "gamma", "beta", "bias")]
+    pad = 4096
+    buf = torch.full((M * 384 + 2 * pad,), float("nan"), dtype=torch.float16, device="cuda")
+    out = buf[pad:pad + M * 384].view(M, 384)
+    ng.fused_norm_gemm(args[0], args[1], *args[2:], eps=case.eps, norm=RMS, act="silu", out=out)
+    y2 = ng.fused_norm_gemm(args[0], args[1], *args[2:], eps=case.eps, norm=RMS, act="silu")
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), y2.view(torch.int16))
+    assert torch.isnan(buf[:pad]).all() and torch.isnan(buf[pad + M * 384:]).all()
+    assert torch.isfinite(out).all()
+
+
+def test_decode_rows_are_independent():
+    """Row m of an M=32 call equals an M=1 call on that row."""
+    import norm_gemm_amd as ng
+    case = synth.make_norm_gemm("rows", 32, 2048, 640, dtype=BF16, norm=RMS, bias=False,
+                                beta=False, eps=1e-6, seed=11)
+    A = case.arrays
+    x, W, g = upload(A["x"], BF16), upload(A["W"], BF16), upload(A["gamma"], BF16)
+    y = ng.fused_norm_gemm(x, W, g, eps=1e-6, norm=RMS)
+    perm = torch.randperm(32, generator=torch.Generator().manual_seed(0)).to("cuda")
+    yp = ng.fused_norm_gemm(x[perm].contiguous(), W, g, eps=1e-6, norm=RMS)
+    rows = [ng.fused_norm_gemm(x[m:m + 1].contiguous(), W, g, eps=1e-6, norm=RMS) for m in (0, 17, 31)]
+    torch.cuda.synchronize()
+    for r, m in zip(rows, (0, 17, 31)):
+        assert_close(to_f64(r)[0], to_f64(y)[m], what=f"row {m}")
+    assert torch.equal(yp.view(torch.int16), y[perm].view(torch.int16))
+
+
+# -------------------------------------------------------------------- FFN
+@pytest.mark.parametrize("M,K,F,N,norm", [(5, 64, 96, 40, NONE), (70, 136, 200, 72, NONE),
+                                          (33, 72, 130, 33, LN), (2, 40, 24, 16, RMS)])
+def test_ffn_small(M, K, F, N, norm):
+    case = synth.make_ffn(f"ffn_{M}x{K}x{F}x{N}", M, K, F, N, norm=norm, gamma=norm != NONE,
+                          beta=norm == LN, b1=True, b2=True, seed=12)
+    check_full(case)
+
+
+@pytest.mark.parametrize("M", [16, 100])
+def test_ffn_equals_two_norm_gemm_calls(M):
+    import norm_gemm_amd as ng
+    case = synth.make_ffn(f"ffn_compose_{M}", M, 128, 320, 96, norm=LN, gamma=True, beta=True,
+                          b1=True, b2=True, seed=13)
+    A = case.arrays
+    u = lambda k: upload(A[k], F16)
+    y = ng.fused_ffn(u("x"), u("W1"), u("W2"), u("gamma"), u("beta"), u("b1"), u("b2"),
+                     eps=1e-5, norm=LN, act="silu")
+    h = ng.fused_norm_gemm(u("x"), u("W1"), u("gamma"), u("beta"), u("b1"), eps=1e-5, norm=LN,
+                           act="silu")
+    y2 = ng.fused_norm_gemm(h, u("W2"), bias=u("b2"), norm=NONE)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+
+
+# ----------------------------------------------------------- full-size workloads
+def check_sampled(case, n_rows, n_cols, tile=128):
+    y = run_case_gpu(case)
+    torch.cuda.synchronize()
+    rows = sample_indices(case.M, n_rows, seed=1, tile=tile)
+    cols = sample_indices(case.N, n_cols, seed=2, tile=tile)
+    ref = oracle.run_case(case, rows=rows, cols=cols)
+    got = to_f64(y)[np.ix_(rows, cols)]
+    err = assert_close(got, ref, what=case.name)
+    print(f"{case.name}: {len(rows)}x{len(cols)} sampled, max rel err {err:.3e}", flush=True)
+    assert torch.isfinite(y).all()
+
+
+def test_full_ln_linear_bias_1024x8192():
+    check_sampled(synth.ln_linear_bias_1024x8192(), 6, 400)
+
+
+def test_full_rms_matmul_silu_512x14336():
+    check_sampled(synth.rms_matmul_silu_512x14336(), 5, 400)
+
+
+def test_full_ffn_silu_512x14336x49152():
+    check_sampled(synth.ffn_silu_512x14336x49152(), 2, 200)
+
+
+@pytest.mark.parametrize("M", [1, 8, 32])
+def test_full_decode_rms_gemm_8192x28672(M):
+    check_sampled(synth.decode_rms_gemm_8192x28672(M), M, 600)
