@@ -32,7 +32,13 @@ ng::GemmArgs make_args(const void *x, const void *gamma, const void *beta, const
 
 int run(const ng::GemmArgs &a, hipStream_t s)
 {
-    hipError_t e = (a.M <= ng::kDecodeMaxM) ? ng::launch_decode(a, s) : ng::launch_prefill(a, s);
+    hipError_t e;
+    if (a.M <= ng::kDecodeMaxM)
+        e = ng::launch_decode(a, s);
+    else if (a.vec)
+        e = ng::launch_prefill_lds(a, s);
+    else
+        e = ng::launch_prefill(a, s);
     return e == hipSuccess ? NG_OK : NG_ERR_HIP;
 }
 

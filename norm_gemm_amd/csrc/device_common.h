@@ -184,4 +184,84 @@ __device__ __forceinline__ void row_stats(const uint16_t *row, int64_t K, float 
     }
 }
 
+
+// ------------------------------------------------------- wait counters
+// s_waitcnt with only vmcnt constrained (expcnt and lgkmcnt left at max);
+// gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14].
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xf) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
+}
+
+// ------------------------------------------- packed-dot row statistics
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef short short2_t __attribute__((ext_vector_type(2)));
+
+// Partial sums of one 8-element chunk for the row statistics, accumulated in
+// fp32 with the packed dot products of gfx950 (v_dot2_f32_f16 / _bf16):
+//   LayerNorm: d = x - shift (shift = the row's first element), s1 += sum d,
+//              s2 += sum d^2;  RMSNorm: s2 += sum x^2.
+// fp16: the shift is a packed fp16 subtraction (exact whenever x and the
+// shift are within a factor of two of each other; otherwise rounded once to
+// 11 bits, which perturbs the variance only at that relative level).
+// bf16: shifted sums in fp32 for LayerNorm, packed bf16 dots for RMSNorm.
+template <int DT, bool LN>
+__device__ __forceinline__ void stats_chunk(const u32x4 &c, uint32_t shift2, float &s1, float &s2)
+{
+    if constexpr (DT == DT_F16) {
+        const half2_t one = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            // copy the element first: hipcc mis-lowers __builtin_bit_cast of an
+            // element of a vector reference (it re-reads element 0)
+            const uint32_t w = c[i];
+            half2_t x = __builtin_bit_cast(half2_t, w);
+            if constexpr (LN) {
+                half2_t d = x - __builtin_bit_cast(half2_t, shift2);
+                s1 = __builtin_amdgcn_fdot2(d, one, s1, false);
+                s2 = __builtin_amdgcn_fdot2(d, d, s2, false);
+            } else {
+                s2 = __builtin_amdgcn_fdot2(x, x, s2, false);
+            }
+        }
+    } else {
+        if constexpr (LN) {
+            const float sh = lo_to_f<DT_BF16>(shift2);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float d0 = lo_to_f<DT_BF16>(c[i]) - sh, d1 = hi_to_f<DT_BF16>(c[i]) - sh;
+                s1 += d0 + d1;
+                s2 = fmaf(d0, d0, fmaf(d1, d1, s2));
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t w = c[i];
+                short2_t x = __builtin_bit_cast(short2_t, w);
+                s2 = __builtin_amdgcn_fdot2_f32_bf16(x, x, s2, false);
+            }
+        }
+    }
+}
+
+// (rs, nmr) from the sums: normalized = x * rs + nmr. LayerNorm:
+// mean = shift + s1/K, var = max(s2/K - (s1/K)^2, 0), rs = 1/sqrt(var+eps),
+// nmr = -mean*rs. RMSNorm: rs = 1/sqrt(s2/K + eps), nmr = 0.
+__device__ __forceinline__ void finish_stats(float s1, float s2, float shift, int64_t K,
+                                             float eps, bool ln, float &rs, float &nmr)
+{
+    const float invK = 1.0f / (float)K;
+    if (ln) {
+        const float md = s1 * invK;
+        const float var = fmaxf(fmaf(-md, md, s2 * invK), 0.0f);
+        rs = rsqrtf(var + eps);
+        nmr = -(shift + md) * rs;
+    } else {
+        rs = rsqrtf(s2 * invK + eps);
+        nmr = 0.0f;
+    }
+}
+
 }  // namespace ng

@@ -16,7 +16,8 @@ struct GemmArgs {
     bool vec;  // K % 8 == 0 and x, W, gamma, beta 16-byte aligned
 };
 
-hipError_t launch_prefill(const GemmArgs &a, hipStream_t s);
+hipError_t launch_prefill(const GemmArgs &a, hipStream_t s);      // any alignment
+hipError_t launch_prefill_lds(const GemmArgs &a, hipStream_t s);  // a.vec only
 hipError_t launch_decode(const GemmArgs &a, hipStream_t s);
 
 constexpr int64_t kDecodeMaxM = 32;
