@@ -34,7 +34,7 @@ int run(const ng::GemmArgs &a, hipStream_t s)
 {
     hipError_t e;
     if (a.M <= ng::kDecodeMaxM)
-        e = ng::launch_decode(a, s);
+        e = a.vec ? ng::launch_decode_lds(a, s) : ng::launch_decode(a, s);
     else if (a.vec)
         e = ng::launch_prefill_lds(a, s);
     else

@@ -195,6 +195,19 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 0xf) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
 }
 
+// -------------------------------------------------------- LDS barrier
+// Workgroup barrier for kernels with direct global->LDS loads in flight:
+// each wave first waits for its own LDS operations (lgkmcnt), then all
+// waves meet. No memory fence on purpose: a workgroup release fence on LDS
+// also waits for every direct load still in flight (they write LDS), which
+// would drain a W prefetch pipeline. Callers that need their own direct
+// loads landed wait on vmcnt before calling. The "memory" clobber keeps the
+// compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // ------------------------------------------- packed-dot row statistics
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef short short2_t __attribute__((ext_vector_type(2)));

@@ -18,7 +18,8 @@ struct GemmArgs {
 
 hipError_t launch_prefill(const GemmArgs &a, hipStream_t s);      // any alignment
 hipError_t launch_prefill_lds(const GemmArgs &a, hipStream_t s);  // a.vec only
-hipError_t launch_decode(const GemmArgs &a, hipStream_t s);
+hipError_t launch_decode(const GemmArgs &a, hipStream_t s);      // any alignment
+hipError_t launch_decode_lds(const GemmArgs &a, hipStream_t s);  // a.vec only
 
 constexpr int64_t kDecodeMaxM = 32;
 

@@ -120,19 +120,6 @@ __device__ __forceinline__ bool tile_of(const TileMap &mp, int w, int r, int G, 
     return true;
 }
 
-// Workgroup barrier for the K loop: this wave's LDS reads and writes are
-// complete (lgkmcnt 0), then all waves meet. Each wave has already waited
-// (vmcnt) for its own direct global->LDS loads of the stage about to be read,
-// so after the barrier every wave's part of that stage is in LDS. No memory
-// fence on purpose: a workgroup release fence on LDS also waits for every
-// direct load still in flight (they write LDS), which would drain the W
-// prefetch pipeline at every step. The "memory" clobber keeps the compiler
-// from moving memory accesses across the barrier.
-__device__ __forceinline__ void lds_barrier()
-{
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
 // Statistics modes of the main kernel.
 enum { ST_NONE = 0, ST_PROLOGUE = 1, ST_FROM_Y = 2 };
 

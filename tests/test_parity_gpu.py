@@ -70,6 +70,30 @@ def test_decode_ragged_shapes(M, N, K, norm, act, dtype):
     check_full(case)
 
 
+# Aligned decode shapes (K % 8 == 0) that select each slab height of the
+# line-streaming decode kernel: 16 * nbk rows of W per workgroup with
+# nbk = clamp(ceil(ceil(N / 16) / 256), 2, 8) on a 256-CU device. The K values
+# leave a ragged last k-block (K % 64 == 8), idle waves (fewer than 8 k-blocks
+# per wave range), odd k-block counts per wave (a tail after the unrolled
+# pairs), and the last case needs more workgroups than CUs.
+DECODE_SLAB_SHAPES = [
+    (1, 9000, 200, RMS, ACT0, BF16, True),      # nbk 3, 4 k-blocks: waves 4..7 idle
+    (16, 13000, 136, LN, SILU, F16, True),      # nbk 4
+    (17, 17000, 64, NONE, ACT0, BF16, False),   # nbk 5, one k-block: only wave 0 works
+    (32, 21000, 520, LN, ACT0, BF16, True),     # nbk 6, 9 k-blocks: wave 4 has one
+    (5, 26000, 1096, RMS, SILU, F16, False),    # nbk 7, 3 k-blocks per wave (pair + tail)
+    (32, 30000, 2056, RMS, ACT0, F16, True),    # nbk 8, 5 k-blocks per wave
+    (9, 40000, 264, LN, SILU, BF16, True),      # nbk 8, 313 workgroups
+]
+
+
+@pytest.mark.parametrize("M,N,K,norm,act,dtype,bias", DECODE_SLAB_SHAPES)
+def test_decode_slab_heights(M, N, K, norm, act, dtype, bias):
+    case = synth.make_norm_gemm(f"decode_slab_{M}x{N}x{K}", M, K, N, dtype=dtype, norm=norm,
+                                act=act, bias=bias, eps=1e-6, seed=M + N // 7 + K)
+    check_full(case)
+
+
 @pytest.mark.parametrize("M", [5, 100])
 @pytest.mark.parametrize("gamma,beta,bias", [(False, False, False), (True, False, True),
                                              (False, True, False)])
