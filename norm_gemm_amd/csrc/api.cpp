@@ -34,7 +34,9 @@ int run(const ng::GemmArgs &a, hipStream_t s)
 {
     hipError_t e;
     if (a.M <= ng::kDecodeMaxM)
-        e = a.vec ? ng::launch_decode_lds(a, s) : ng::launch_decode(a, s);
+        e = !a.vec ? ng::launch_decode(a, s)
+                   : (ng::decode_wide_fits(a) ? ng::launch_decode_wide(a, s)
+                                              : ng::launch_decode_lds(a, s));
     else if (a.vec)
         e = ng::launch_prefill_lds(a, s);
     else

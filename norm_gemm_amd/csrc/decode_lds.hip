@@ -151,7 +151,7 @@ __global__ __launch_bounds__(64 * kNW) void decode_lds_kernel(
     const bool has_work = kb0 < kb1;
     if (has_work) {
         load_x(ic<0>{}, kb0);
-        __builtin_amdgcn_sched_barrier(0);   // keep x ahead of the blocks
+        issue_fence(x, gamma, beta);   // keep x ahead of the blocks
         static_for<0, D>([&](auto NB) { issue_block(NB, kb0); });
     }
 
@@ -164,7 +164,7 @@ __global__ __launch_bounds__(64 * kNW) void decode_lds_kernel(
     if constexpr (AFFINE) {
         for (int m = wave; m < M; m += kNW) {
             float a, b;
-            row_stats<DT, true>(x + (int64_t)m * K, K, eps, norm, lane, a, b);
+            row_stats_wide<DT>(x + (int64_t)m * K, K, eps, norm, lane, a, b);
             if (lane == 0) {
                 s_rs[m] = a;
                 s_mu[m] = b;
@@ -236,7 +236,7 @@ __global__ __launch_bounds__(64 * kNW) void decode_lds_kernel(
         // that many leaves the D prefetched blocks in flight.
         if constexpr (next) {
             load_x(ic<set ^ 1>{}, kb + 1);
-            __builtin_amdgcn_sched_barrier(0);
+            issue_fence(x, gamma, beta);
             wait_vmcnt<2 * D + XL>();
         } else {
             wait_vmcnt<2 * D>();
@@ -248,7 +248,7 @@ __global__ __launch_bounds__(64 * kNW) void decode_lds_kernel(
             constexpr int nb_next = (nb + D) % NBK;
             // the refill of slot nb_next (read at the step before) stays
             // behind that step's MFMAs, hence behind its LDS reads
-            __builtin_amdgcn_sched_barrier(0);
+            issue_fence(x, gamma, beta);
             issue_block(ic<nb_next>{}, nb + D >= NBK ? kb + 1 : kb);
             if constexpr (next && nb < D)
                 wait_vmcnt<2 * D + XL>();

@@ -195,6 +195,22 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 0xf) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
 }
 
+// --------------------------------------------------------- issue fence
+// Keeps loads through the given pointers, and all other memory operations,
+// on their side of this point in program order. The pointers go into a
+// volatile asm that clobbers memory, so at the IR level that asm may write
+// through them and loads cannot be sunk or hoisted across it (a memory
+// clobber alone does not bind __restrict__ arguments that never escape, and
+// sched_barrier does not touch memory at the IR level); sched_barrier then
+// stops the machine scheduler. Kernels whose explicit vmcnt waits count the
+// loads issued between two points rely on it.
+__device__ __forceinline__ void issue_fence(const void *a, const void *b = nullptr,
+                                            const void *c = nullptr)
+{
+    asm volatile("" ::"s"(a), "s"(b), "s"(c) : "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 // -------------------------------------------------------- LDS barrier
 // Workgroup barrier for kernels with direct global->LDS loads in flight:
 // each wave first waits for its own LDS operations (lgkmcnt), then all
@@ -274,6 +290,51 @@ __device__ __forceinline__ void finish_stats(float s1, float s2, float shift, in
     } else {
         rs = rsqrtf(s2 * invK + eps);
         nmr = 0.0f;
+    }
+}
+
+// Statistics of one row in the (rs, mu) form -- normalized = (x - mu) * rs --
+// for 16-byte aligned rows with K % 8 == 0, one wave per row. Each lane
+// issues its 16 chunks of every 1024-chunk stretch of the row before
+// accumulating any, so a row of up to 8192 elements costs one memory round
+// trip (the plain loop of row_stats waits for each chunk in turn). Sums as in
+// stats_chunk (shift = the row's first element for LayerNorm).
+template <int DT>
+__device__ __forceinline__ void row_stats_wide(const uint16_t *row, int K, float eps, int norm,
+                                               int lane, float &rs, float &mu)
+{
+    constexpr int UNR = 16;
+    const bool ln = norm == NORM_LAYERNORM;
+    const uint32_t s0 = row[0];
+    const uint32_t shift2 = ln ? (s0 | (s0 << 16)) : 0u;
+    float s1 = 0.0f, s2 = 0.0f;
+    const int nchunk = K / 8;
+    for (int c0 = 0; c0 < nchunk; c0 += 64 * UNR) {
+        u32x4 v[UNR];
+#pragma unroll
+        for (int u = 0; u < UNR; ++u)
+            v[u] = ldg128(row + (int64_t)min(c0 + u * 64 + lane, nchunk - 1) * 8);
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+            if (c0 + u * 64 + lane < nchunk) {
+                if (ln)
+                    stats_chunk<DT, true>(v[u], shift2, s1, s2);
+                else
+                    stats_chunk<DT, false>(v[u], shift2, s1, s2);
+            }
+        }
+    }
+    s1 = wave_sum(s1);
+    s2 = wave_sum(s2);
+    const float invK = 1.0f / (float)K;
+    if (ln) {
+        const float md = s1 * invK;
+        const float var = fmaxf(fmaf(-md, md, s2 * invK), 0.0f);
+        rs = rsqrtf(var + eps);
+        mu = bits_to_f<DT>((uint16_t)s0) + md;
+    } else {
+        rs = rsqrtf(s2 * invK + eps);
+        mu = 0.0f;
     }
 }
 

@@ -20,6 +20,8 @@ hipError_t launch_prefill(const GemmArgs &a, hipStream_t s);      // any alignme
 hipError_t launch_prefill_lds(const GemmArgs &a, hipStream_t s);  // a.vec only
 hipError_t launch_decode(const GemmArgs &a, hipStream_t s);      // any alignment
 hipError_t launch_decode_lds(const GemmArgs &a, hipStream_t s);  // a.vec only
+hipError_t launch_decode_wide(const GemmArgs &a, hipStream_t s); // a.vec and decode_wide_fits
+bool decode_wide_fits(const GemmArgs &a);  // M <= 16, N >= 16, 32-bit slab offsets
 
 constexpr int64_t kDecodeMaxM = 32;
 

@@ -84,6 +84,11 @@ DECODE_SLAB_SHAPES = [
     (5, 26000, 1096, RMS, SILU, F16, False),    # nbk 7, 3 k-blocks per wave (pair + tail)
     (32, 30000, 2056, RMS, ACT0, F16, True),    # nbk 8, 5 k-blocks per wave
     (9, 40000, 264, LN, SILU, BF16, True),      # nbk 8, 313 workgroups
+    # M <= 16 kernel: rows past 8 and rows longer than 8192 take the second
+    # statistics pass; N = 17 moves the last 16-row slab back onto row 1
+    (12, 2056, 8200, LN, SILU, F16, True),
+    (2, 17, 1024, RMS, ACT0, BF16, False),
+    (16, 4100, 16384, RMS, SILU, BF16, True),
 ]
 
 
