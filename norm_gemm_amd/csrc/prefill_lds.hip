@@ -40,15 +40,18 @@ namespace ng {
 namespace {
 
 constexpr int BM = 128, BN = 256, BK = 64;
-constexpr int NWAVE = 4, THREADS = 64 * NWAVE;
+constexpr int NWAVE = 8, THREADS = 64 * NWAVE;
 constexpr int CPR = BK / 8;                      // 16-byte chunks per tile row
 constexpr int A_CH = BM * CPR / THREADS;         // A chunks per thread per K step (4)
 constexpr int A_ROWS_PER_PASS = THREADS / CPR;   // 32
 constexpr int B_DMA = BN * CPR / THREADS;        // W direct loads per lane per K step (8)
 constexpr int A_TILE = BM * CPR, B_TILE = BN * CPR;   // in 16-byte chunks
 static_assert(2 * A_TILE * 16 + 4 * B_TILE * 16 == 160 * 1024, "LDS budget");
-constexpr int WM = 64, WN = 128;                 // wave tile (m x n)
-constexpr int FM = WM / 32, FN = WN / 32;        // 32x32 blocks per wave (2 x 4)
+constexpr int WM = 64, WN = 64;                  // wave tile (m x n)
+constexpr int WGM = BM / WM, WGN = BN / WN;      // wave grid (2 x 4)
+constexpr int FM = WM / 32, FN = WN / 32;        // 32x32 blocks per wave (2 x 2)
+constexpr int B_RPW = BN / NWAVE;                // W rows loaded per wave per K step
+static_assert(WGM * WGN == NWAVE && B_RPW % 8 == 0 && B_DMA * 8 == B_RPW, "wave split");
 
 static_assert(A_CH * THREADS == BM * CPR && B_DMA * THREADS == BN * CPR, "tile split");
 static_assert(64 * 32 <= B_TILE, "half-tile epilogue staging fits one W stage");
@@ -99,25 +102,20 @@ struct TileMap {
     int xcd;            // 1: XCD-grouped assignment (see file comment)
 };
 
-// Tile t of workgroup w in round r; false when the workgroup is done.
-__device__ __forceinline__ bool tile_of(const TileMap &mp, int w, int r, int G, int &mb, int &nt)
+// Tile of workgroup b (one tile per workgroup, T workgroups). XCD-grouped:
+// workgroup b runs on XCD b % 8, and the j-th workgroup of an XCD takes row
+// block j % tm of column block (b % 8) * (tn / 8) + j / tm, so the workgroups
+// an XCD runs together cover every row block of a few W column blocks.
+__device__ __forceinline__ void tile_of(const TileMap &mp, int b, int &mb, int &nt)
 {
     if (mp.xcd) {
-        const int P = G >> 3, x = w & 7, j = w >> 3;
-        const int per_xcd = mp.tm * (mp.tn >> 3);
-        const int L = r * P + j;
-        if (L >= per_xcd)
-            return false;
-        mb = L % mp.tm;
-        nt = x * (mp.tn >> 3) + L / mp.tm;
-        return true;
+        const int x = b & 7, j = b >> 3;
+        mb = j % mp.tm;
+        nt = x * (mp.tn >> 3) + j / mp.tm;
+        return;
     }
-    const int t = w + r * G;
-    if (t >= mp.T)
-        return false;
-    mb = t % mp.tm;
-    nt = t / mp.tm;
-    return true;
+    mb = b % mp.tm;
+    nt = b / mp.tm;
 }
 
 // Statistics modes of the main kernel.
@@ -216,12 +214,14 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;       // 2 x 2 waves
+    const int wm = wave / WGN, wn = wave % WGN;
     const int lrow = lane & 31, lk = lane >> 5;
     const int cc = tid % CPR, r0 = tid / CPR;      // A chunk coordinates
+    // rows r0 + i * A_ROWS_PER_PASS share the swizzle (A_ROWS_PER_PASS % 16 == 0)
+    static_assert(A_ROWS_PER_PASS % 16 == 0, "one swizzle for a thread's A rows");
+    const int a_woff = r0 * CPR + swz(r0, cc);
     const int nk = (K + BK - 1) / BK;
     const bool k_tail = (K % BK) != 0;
-    const int G = gridDim.x;
     // gamma / beta are read unconditionally (a valid stand-in pointer when
     // absent) so that the K loop has no branches around its loads
     const bool has_g = gamma != nullptr, has_b = beta != nullptr;
@@ -236,15 +236,13 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
         rnmr[i] = 0.0f;
     }
 
-    int cur_mb = -1;
-    for (int round = 0;; ++round) {
+    {
         int mb, nt;
-        if (!tile_of(mp, blockIdx.x, round, G, mb, nt))
-            break;
+        tile_of(mp, blockIdx.x, mb, nt);
         const int m0 = mb * BM, n0 = nt * BN;
 
         // ---- W: direct HBM -> LDS loads of K step kt into stage buffer dst.
-        // DMA instruction i of this wave fills rows wave*64 + i*8 .. +7; lane l
+        // DMA instruction i of this wave fills rows wave*B_RPW + i*8 .. +7; lane l
         // lands at chunk position l, i.e. row +l/8, physical chunk l%8, which
         // holds logical chunk swz(row, l%8). Rows past N re-read row N-1
         // (their outputs are discarded); steps past the last re-read the last
@@ -254,7 +252,7 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
         int wch[B_DMA];
 #pragma unroll
         for (int i = 0; i < B_DMA; ++i) {
-            const int row = wave * 64 + i * 8 + (lane >> 3);
+            const int row = wave * B_RPW + i * 8 + (lane >> 3);
             wch[i] = swz(row, lane & 7);
             wrow[i] = W + (int64_t)min(n0 + row, N - 1) * K;
         }
@@ -265,14 +263,14 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
                 const int k = kt * BK + wch[i] * 8;
                 __builtin_amdgcn_global_load_lds(
                     (const void *)(wrow[i] + (k < K ? k : 0)),
-                    (__attribute__((address_space(3))) void *)&dst[(wave * 64 + i * 8) * CPR], 16, 0,
-                    0);
+                    (__attribute__((address_space(3))) void *)&dst[(wave * B_RPW + i * 8) * CPR], 16,
+                    0, 0);
             }
         };
         auto fix_tail = [&](u32x4 *dst) {
 #pragma unroll
             for (int i = 0; i < B_DMA; ++i) {
-                const int row = wave * 64 + i * 8 + (lane >> 3);
+                const int row = wave * B_RPW + i * 8 + (lane >> 3);
                 if ((nk - 1) * BK + wch[i] * 8 >= K)
                     dst[row * CPR + (lane & 7)] = u32x4{0u, 0u, 0u, 0u};
             }
@@ -319,7 +317,7 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
                 rnmr[i] = __builtin_bit_cast(float, pk.y);
             }
         } else if constexpr (STATS == ST_PROLOGUE) {
-            if (mb != cur_mb) {
+            {
                 // one wave per row, 4 rows at a time, reduced in fp32; staged
                 // through the second x stage (free until the first K step)
                 float *s_rs = reinterpret_cast<float *>(A1);
@@ -369,7 +367,6 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
                     rnmr[i] = s_nmr[r0 + i * A_ROWS_PER_PASS];
                 }
                 __syncthreads();
-                cur_mb = mb;
             }
         }
 
@@ -388,17 +385,15 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
                 }
 #pragma unroll
                 for (int i = 0; i < A_CH; ++i) {
-                    const int r = r0 + i * A_ROWS_PER_PASS;
                     const u32x4 v = normalize_chunk<DT>(ra[set][i], rrs[i], rnmr[i], g, b);
-                    dst[r * CPR + swz(r, cc)] = (kin && rlive[i]) ? v : u32x4{0u, 0u, 0u, 0u};
+                    dst[a_woff + i * A_ROWS_PER_PASS * CPR] =
+                        (kin && rlive[i]) ? v : u32x4{0u, 0u, 0u, 0u};
                 }
             } else {
 #pragma unroll
-                for (int i = 0; i < A_CH; ++i) {
-                    const int r = r0 + i * A_ROWS_PER_PASS;
-                    dst[r * CPR + swz(r, cc)] =
+                for (int i = 0; i < A_CH; ++i)
+                    dst[a_woff + i * A_ROWS_PER_PASS * CPR] =
                         (kin && rlive[i]) ? ra[set][i] : u32x4{0u, 0u, 0u, 0u};
-                }
             }
         };
 
@@ -420,19 +415,20 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
 #pragma unroll
                 for (int e = 0; e < 16; ++e) acc[j][i][e] = 0.0f;
 
+        // Operand chunk of this lane for sub-step kk: rows 32 apart share the
+        // swizzle, so one offset per sub-step (plus compile-time row and
+        // stage offsets) addresses every fragment of every stage.
         u32x4 wf[2][FN], xf[2][FM];
         auto read_frags = [&](const u32x4 *Ac, const u32x4 *Bc, int kk, int buf) {
-            const int ch = kk * 2 + lk;
+            const int sw = swz(lrow, kk * 2 + lk);
+            const int aoff = (wm * WM + lrow) * CPR + sw;
+            const int boff = (wn * WN + lrow) * CPR + sw;
 #pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int r = wn * WN + j * 32 + lrow;
-                wf[buf][j] = Bc[r * CPR + swz(r, ch)];
-            }
+            for (int j = 0; j < FN; ++j)
+                wf[buf][j] = Bc[boff + j * 32 * CPR];
 #pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                const int r = wm * WM + i * 32 + lrow;
-                xf[buf][i] = Ac[r * CPR + swz(r, ch)];
-            }
+            for (int i = 0; i < FM; ++i)
+                xf[buf][i] = Ac[aoff + i * 32 * CPR];
         };
         auto mfmas = [&](int buf) {
 #pragma unroll
@@ -516,9 +512,10 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
             }
         }
         __syncthreads();
+        constexpr int ROWS_PER_PASS = THREADS / 32;
 #pragma unroll 4
-        for (int p = 0; p < BM / 8; ++p) {
-            const int row = p * 8 + (tid >> 5), ch = tid & 31;
+        for (int p = 0; p < BM / ROWS_PER_PASS; ++p) {
+            const int row = p * ROWS_PER_PASS + (tid >> 5), ch = tid & 31;
             const int m = m0 + row, n = n0 + ch * 8;
             const u32x4 *src = row < 64 ? B0 : B1;
             const int rl = row & 63;
@@ -550,8 +547,7 @@ hipError_t launch_t(const GemmArgs &a, hipStream_t s)
     mp.tm = (int)((a.M + BM - 1) / BM);
     mp.tn = (int)((a.N + BN - 1) / BN);
     mp.T = mp.tm * mp.tn;
-    int G = mp.T < cus ? mp.T : cus;
-    mp.xcd = (G == cus && cus % 8 == 0 && mp.tn % 8 == 0 && (cus / 8) % mp.tm == 0) ? 1 : 0;
+    mp.xcd = (cus % 8 == 0 && mp.tn % 8 == 0) ? 1 : 0;
     const int vec_out = (a.N % 8 == 0 && ((uintptr_t)a.y & 15u) == 0) ? 1 : 0;
     if constexpr (STATS == ST_FROM_Y) {
         hipLaunchKernelGGL((row_stats_to_y_kernel<DT>), dim3((unsigned)((a.M + 3) / 4)), dim3(256),
@@ -561,7 +557,7 @@ hipError_t launch_t(const GemmArgs &a, hipStream_t s)
         if (e != hipSuccess)
             return e;
     }
-    hipLaunchKernelGGL((prefill_lds_kernel<DT, STATS>), dim3(G), dim3(THREADS), 0, s,
+    hipLaunchKernelGGL((prefill_lds_kernel<DT, STATS>), dim3(mp.T), dim3(THREADS), 0, s,
                        (const uint16_t *)a.x, (const uint16_t *)a.gamma, (const uint16_t *)a.beta,
                        (const uint16_t *)a.W, (const uint16_t *)a.bias, (uint16_t *)a.y, (int)a.M,
                        (int)a.N, (int)a.K, a.eps, a.norm, a.act, mp, vec_out);
