@@ -195,6 +195,30 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 0xf) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
 }
 
+// ------------------------------------------------- explicit direct load
+// One 16-byte-per-lane direct load HBM -> LDS (global_load_lds_dwordx4,
+// address = scalar base + 32-bit vector offset; lane l writes LDS byte
+// address lds + 16 l through M0), issued as inline asm. The compiler does
+// not see it as a load: it inserts no waits for it, and its own waits for
+// other loads only get stricter. The caller orders it with explicit vmcnt
+// waits and barriers; the "memory" clobber keeps other memory accesses on
+// their side of it. M0 is only used by these statements in the kernels
+// that call it.
+__device__ __forceinline__ void dma16(const void *sbase, uint32_t voff, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(sbase), "s"(lds)
+                 : "memory", "m0");
+}
+
+// LDS byte address of a __shared__ object element, as a wave-uniform value
+__device__ __forceinline__ uint32_t lds_addr(const void *p)
+{
+    return __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p);
+}
+
 // --------------------------------------------------------- issue fence
 // Keeps loads through the given pointers, and all other memory operations,
 // on their side of this point in program order. The pointers go into a

@@ -4,22 +4,26 @@
 // normalized tile kept on chip, weights fetched while the statistics are
 // computed, aligned contiguous accesses).
 //
-// Persistent workgroups of 4 waves, one per CU, each walking a list of
-// 128 x 256 output tiles that share one 128-row block of x:
-//   prologue  W tiles for the first two K steps are requested straight into
-//             LDS; the 4 waves reduce the statistics of the block's 128 rows
-//             (one pass, packed dot products accumulating in fp32) unless the
-//             previous tile had the same rows.
-//   K loop    BK = 64. W: HBM -> LDS by direct 128-bit loads (no registers),
-//             three stages in flight. x: HBM -> registers -> normalize + affine
-//             in fp32 (x*rs + nmr, then *gamma + beta, mixed-precision FMAs)
-//             -> one RNE rounding -> LDS, two stages. The normalized x lives
-//             only in registers and LDS.
-//   MFMA      v_mfma_f32_32x32x16 with W as the first operand and normalized
-//             x as the second, so each 32x32 result block is y^T: lane l holds
-//             output row m = l % 32 and four consecutive output columns.
-//   epilogue  + bias, optional SiLU, one rounding, staged through LDS into
-//             row-major order and written with 128-bit stores.
+// One workgroup of 8 waves per 128 x 256 output tile, one workgroup per CU
+// (150 KB of LDS). Each wave computes a 64 x 64 block of the tile.
+//   statistics  a separate pass reduces each row of x once (one pass, fp32
+//               sum and sum of squares) and leaves (1/sigma, -mu/sigma) in
+//               the tile's own rows of y, which the main kernel reads before
+//               it writes them (an in-kernel prologue is used when y cannot
+//               serve as scratch).
+//   K loop      BK = 64, three LDS stages, loads two steps ahead. x, gamma,
+//               beta and W go HBM -> LDS by direct 128-bit loads (no
+//               registers), issued one after each pair of MFMAs so that the
+//               load unit stays busy while the matrix cores run. Halfway
+//               through step k each lane normalizes the x chunks of step k + 1
+//               that its own loads brought in (fp16: packed fp16 arithmetic;
+//               bf16: fp32), in place, so the normalized x lives only in LDS.
+//   MFMA        v_mfma_f32_32x32x16 with W as the first operand and normalized
+//               x as the second, so each 32x32 result block is y^T: lane l
+//               holds output row m = l % 32 and four consecutive columns.
+//               Fragments of the next sub-step are read ahead.
+//   epilogue    + bias, optional SiLU, one rounding, staged through LDS into
+//               row-major order and written with 128-bit stores.
 //
 // Workgroups are dealt to the 8 XCDs round-robin. When the shape allows, the
 // tiles are assigned so that the 32 workgroups of one XCD work at the same
@@ -42,18 +46,22 @@ namespace {
 constexpr int BM = 128, BN = 256, BK = 64;
 constexpr int NWAVE = 8, THREADS = 64 * NWAVE;
 constexpr int CPR = BK / 8;                      // 16-byte chunks per tile row
-constexpr int A_CH = BM * CPR / THREADS;         // A chunks per thread per K step (4)
-constexpr int A_ROWS_PER_PASS = THREADS / CPR;   // 32
-constexpr int B_DMA = BN * CPR / THREADS;        // W direct loads per lane per K step (8)
+constexpr int B_DMA = BN * CPR / THREADS;        // W direct loads per lane per K step (4)
 constexpr int A_TILE = BM * CPR, B_TILE = BN * CPR;   // in 16-byte chunks
-static_assert(2 * A_TILE * 16 + 4 * B_TILE * 16 == 160 * 1024, "LDS budget");
+constexpr int NSTAGE = 3;                        // pipeline stages (loads 2 steps ahead)
+constexpr int G_CH = 128;                        // gamma / beta stage: 2 x 64 chunks
+constexpr int A_DMA = BM * CPR / THREADS;        // x direct loads per lane per K step (2)
+constexpr int A_RPW = BM / NWAVE;                // x rows loaded per wave per K step
+constexpr int A_IST = BM / A_DMA;                // rows between a lane's x rows (64)
+static_assert(NSTAGE * (A_TILE + B_TILE + G_CH) * 16 <= 160 * 1024, "LDS budget");
+static_assert(A_DMA * 8 == A_RPW && A_IST % 16 == 0, "x rows per wave; one swizzle per lane");
 constexpr int WM = 64, WN = 64;                  // wave tile (m x n)
 constexpr int WGM = BM / WM, WGN = BN / WN;      // wave grid (2 x 4)
 constexpr int FM = WM / 32, FN = WN / 32;        // 32x32 blocks per wave (2 x 2)
 constexpr int B_RPW = BN / NWAVE;                // W rows loaded per wave per K step
 static_assert(WGM * WGN == NWAVE && B_RPW % 8 == 0 && B_DMA * 8 == B_RPW, "wave split");
 
-static_assert(A_CH * THREADS == BM * CPR && B_DMA * THREADS == BN * CPR, "tile split");
+static_assert(B_DMA * THREADS == BN * CPR, "tile split");
 static_assert(64 * 32 <= B_TILE, "half-tile epilogue staging fits one W stage");
 
 // ds_read_b128 is served 16 lanes (256 bytes, all 64 banks) at a time; with
@@ -71,19 +79,6 @@ __device__ __forceinline__ floatx16 mfma32(const u32x4 &a, const u32x4 &b, const
     else
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-
-// One normalized chunk: a = (x * rs + nmr) * g + b in fp32, one rounding.
-template <int DT>
-__device__ __forceinline__ u32x4 normalize_chunk(const u32x4 &raw, float rs, float nmr,
-                                                 const float *g, const float *b)
-{
-    float f[8];
-    unpack8<DT>(raw, f);
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-        f[e] = fmaf(fmaf(f[e], rs, nmr), g[e], b[e]);
-    return pack8<DT>(f);
 }
 
 // NORM_GEMM_STATS=prologue selects the in-kernel statistics prologue instead of
@@ -176,7 +171,10 @@ __global__ __launch_bounds__(256) void row_stats_to_y_kernel(const uint16_t *__r
         *reinterpret_cast<uint2 *>(y + (int64_t)m * N + (int64_t)t * BN) = pk;
 }
 
-template <int DT, int STATS>
+// GB: bit 0 gamma present, bit 1 beta present (with STATS != ST_NONE);
+// KT: K % 64 != 0 (the last K step is ragged); LN: LayerNorm (else RMSNorm,
+// with STATS != ST_NONE).
+template <int DT, int STATS, int GB, bool KT, bool LN>
 __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ gamma,
     const uint16_t *__restrict__ beta, const uint16_t *__restrict__ W,
@@ -184,359 +182,535 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
     float eps, int norm, int act, TileMap mp, int vec_out)
 {
     constexpr bool AFFINE = STATS != ST_NONE;
+    constexpr bool HG = AFFINE && (GB & 1), HB = AFFINE && (GB & 2);
+    constexpr int G_DMA = (HG ? 1 : 0) + (HB ? 1 : 0);
+    constexpr int LPS = B_DMA + A_DMA + G_DMA;     // direct loads per lane per K step
     // One LDS object per pipeline stage, so that the compiler can tell the
     // stage being filled by direct loads from the stages being read.
-    // 2 x 16 KB (x) + 4 x 32 KB (W) = 160 KB, the whole LDS of a CU.
-    __shared__ u32x4 A0[A_TILE], A1[A_TILE];
-    __shared__ u32x4 B0[B_TILE], B1[B_TILE], B2[B_TILE], B3[B_TILE];
-    // stage buffers by compile-time index
+    // x stage s holds the x tile followed by the gamma / beta chunks of the
+    // same K step (one object per stage: at most six LDS objects are filled
+    // by direct loads, which the compiler still tracks one by one)
+    __shared__ u32x4 A0[A_TILE + G_CH], A1[A_TILE + G_CH], A2[A_TILE + G_CH];
+    __shared__ u32x4 B0[B_TILE], B1[B_TILE], B2[B_TILE];
     auto Ast = [&](auto sc) -> u32x4 * {
-        if constexpr ((decltype(sc)::value & 1) == 0)
+        constexpr int i = decltype(sc)::value % NSTAGE;
+        if constexpr (i == 0)
             return A0;
-        else
+        else if constexpr (i == 1)
             return A1;
+        else
+            return A2;
     };
     auto Bst = [&](auto sc) -> u32x4 * {
-        constexpr int i = decltype(sc)::value & 3;
+        constexpr int i = decltype(sc)::value % NSTAGE;
         if constexpr (i == 0)
             return B0;
         else if constexpr (i == 1)
             return B1;
-        else if constexpr (i == 2)
-            return B2;
         else
-            return B3;
+            return B2;
     };
+    auto Gst = [&](auto sc) -> u32x4 * { return Ast(sc) + A_TILE; };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
-    using I3 = std::integral_constant<int, 3>;
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WGN, wn = wave % WGN;
     const int lrow = lane & 31, lk = lane >> 5;
-    const int cc = tid % CPR, r0 = tid / CPR;      // A chunk coordinates
-    // rows r0 + i * A_ROWS_PER_PASS share the swizzle (A_ROWS_PER_PASS % 16 == 0)
-    static_assert(A_ROWS_PER_PASS % 16 == 0, "one swizzle for a thread's A rows");
-    const int a_woff = r0 * CPR + swz(r0, cc);
     const int nk = (K + BK - 1) / BK;
-    const bool k_tail = (K % BK) != 0;
-    // gamma / beta are read unconditionally (a valid stand-in pointer when
-    // absent) so that the K loop has no branches around its loads
-    const bool has_g = gamma != nullptr, has_b = beta != nullptr;
-    const uint16_t *gp = has_g ? gamma : x;
-    const uint16_t *bp = has_b ? beta : x;
+    constexpr bool k_tail = KT;
 
-    // (rs, nmr) of this thread's 4 x rows; kept across tiles of one row block
-    float rrs[A_CH], rnmr[A_CH];
+    int mb, nt;
+    tile_of(mp, blockIdx.x, mb, nt);
+    const int m0 = mb * BM, n0 = nt * BN;
+
+    // ---- direct HBM -> LDS loads. Instruction i of a wave fills 8 tile rows
+    // (x: i*A_IST + wave*8 .., W: wave*B_RPW + i*8 ..); lane l lands at chunk
+    // position l, i.e. row +l/8, physical chunk l%8, which holds logical chunk
+    // swz(row, l%8). Rows past M or N re-read the last row (x rows are zeroed
+    // when normalized, W rows' outputs are discarded); steps past the last
+    // re-read the last step (never consumed).
+    // Addressing: a uniform base (tile origin + K step, scalar registers)
+    // plus a per-lane 32-bit byte offset that is fixed for the whole tile, so
+    // no address register is rewritten while its load is in flight (the
+    // compiler would wait for the load before reusing it). The last K step
+    // of a ragged K has its own fixed offsets: chunks past K re-read the
+    // row's last valid chunk (in bounds) and are zeroed once landed.
+    const int kl = (nk - 1) * BK;                     // first k of the last step
+    const int clast = (K - kl + 7) / 8 - 1;           // last valid chunk in it
+    auto tail_chunk = [&](int c) { return kl + c * 8 < K ? c : clast; };
+    int wch[B_DMA], ach[A_DMA];
+    uint32_t woff[B_DMA], woff_t[B_DMA], aoff_g[A_DMA], aoff_t[A_DMA];
+    bool alive[A_DMA];
+    const uint16_t *wtile = W + (int64_t)n0 * K;
+    const uint16_t *xtile = x + (int64_t)m0 * K;
 #pragma unroll
-    for (int i = 0; i < A_CH; ++i) {
+    for (int i = 0; i < B_DMA; ++i) {
+        const int row = wave * B_RPW + i * 8 + (lane >> 3);
+        wch[i] = swz(row, lane & 7);
+        const uint32_t rb = (uint32_t)(min(n0 + row, N - 1) - n0) * (uint32_t)K;
+        woff[i] = (rb + wch[i] * 8) * 2u;
+        woff_t[i] = (rb + tail_chunk(wch[i]) * 8) * 2u;
+    }
+#pragma unroll
+    for (int i = 0; i < A_DMA; ++i) {
+        const int row = i * A_IST + wave * 8 + (lane >> 3);
+        ach[i] = swz(row, lane & 7);
+        alive[i] = m0 + row < M;
+        const uint32_t rb = (uint32_t)(min(m0 + row, M - 1) - m0) * (uint32_t)K;
+        aoff_g[i] = (rb + ach[i] * 8) * 2u;
+        aoff_t[i] = (rb + tail_chunk(ach[i]) * 8) * 2u;
+    }
+    const uint32_t goff = (lane & 7) * 16u, goff_t = tail_chunk(lane & 7) * 16u;
+    auto issue = [&](int kt, u32x4 *As, u32x4 *Bs, u32x4 *Gs) {
+        kt = min(kt, nk - 1);
+        const char *wb = reinterpret_cast<const char *>(wtile) + (size_t)kt * (BK * 2);
+        const char *xb = reinterpret_cast<const char *>(xtile) + (size_t)kt * (BK * 2);
+        const char *gb = reinterpret_cast<const char *>(gamma) + (size_t)kt * (BK * 2);
+        const char *bb = reinterpret_cast<const char *>(beta) + (size_t)kt * (BK * 2);
+        // direct loads as explicit asm (see dma16): the compiler inserts no
+        // waits of its own in the K loop; the step's vmcnt wait and barrier
+        // order everything
+        // x, gamma, beta, then W: the order of the load slots of the K loop
+        auto go = [&](const uint32_t *wo, const uint32_t *ao, uint32_t go_) {
+#pragma unroll
+            for (int i = 0; i < A_DMA; ++i)
+                dma16(xb, ao[i], lds_addr(&As[(i * A_IST + wave * 8) * CPR]));
+            // gamma chunks 0-7 at positions 0-7 (lanes 8-63 repeat them), beta
+            // chunks at 64 + 0-7
+            if constexpr (HG)
+                dma16(gb, go_, lds_addr(Gs));
+            if constexpr (HB)
+                dma16(bb, go_, lds_addr(&Gs[64]));
+#pragma unroll
+            for (int i = 0; i < B_DMA; ++i)
+                dma16(wb, wo[i], lds_addr(&Bs[(wave * B_RPW + i * 8) * CPR]));
+        };
+        if constexpr (!KT) {
+            go(woff, aoff_g, goff);
+        } else {
+            if (kt < nk - 1)
+                go(woff, aoff_g, goff);
+            else
+                go(woff_t, aoff_t, goff_t);
+        }
+    };
+
+    // (rs, nmr) of the rows of this lane's x chunks
+    float rrs[A_DMA], rnmr[A_DMA];
+#pragma unroll
+    for (int i = 0; i < A_DMA; ++i) {
         rrs[i] = 1.0f;
         rnmr[i] = 0.0f;
     }
-
-    {
-        int mb, nt;
-        tile_of(mp, blockIdx.x, mb, nt);
-        const int m0 = mb * BM, n0 = nt * BN;
-
-        // ---- W: direct HBM -> LDS loads of K step kt into stage buffer dst.
-        // DMA instruction i of this wave fills rows wave*B_RPW + i*8 .. +7; lane l
-        // lands at chunk position l, i.e. row +l/8, physical chunk l%8, which
-        // holds logical chunk swz(row, l%8). Rows past N re-read row N-1
-        // (their outputs are discarded); steps past the last re-read the last
-        // step (never consumed); chunks past K read the row's first chunk and
-        // are zeroed once landed (fix_tail).
-        const uint16_t *wrow[B_DMA];
-        int wch[B_DMA];
+    if constexpr (STATS == ST_FROM_Y) {
+        // statistics left by the statistics pass in this tile's own rows
 #pragma unroll
-        for (int i = 0; i < B_DMA; ++i) {
-            const int row = wave * B_RPW + i * 8 + (lane >> 3);
-            wch[i] = swz(row, lane & 7);
-            wrow[i] = W + (int64_t)min(n0 + row, N - 1) * K;
+        for (int i = 0; i < A_DMA; ++i) {
+            const int m = min(m0 + i * A_IST + wave * 8 + (lane >> 3), M - 1);
+            const uint2 pk = *reinterpret_cast<const uint2 *>(y + (int64_t)m * N + n0);
+            rrs[i] = __builtin_bit_cast(float, pk.x);
+            rnmr[i] = __builtin_bit_cast(float, pk.y);
         }
-        auto issue_b = [&](int kt, u32x4 *dst) {
-            kt = min(kt, nk - 1);
-#pragma unroll
-            for (int i = 0; i < B_DMA; ++i) {
-                const int k = kt * BK + wch[i] * 8;
-                __builtin_amdgcn_global_load_lds(
-                    (const void *)(wrow[i] + (k < K ? k : 0)),
-                    (__attribute__((address_space(3))) void *)&dst[(wave * B_RPW + i * 8) * CPR], 16,
-                    0, 0);
-            }
-        };
-        auto fix_tail = [&](u32x4 *dst) {
-#pragma unroll
-            for (int i = 0; i < B_DMA; ++i) {
-                const int row = wave * B_RPW + i * 8 + (lane >> 3);
-                if ((nk - 1) * BK + wch[i] * 8 >= K)
-                    dst[row * CPR + (lane & 7)] = u32x4{0u, 0u, 0u, 0u};
-            }
-        };
-
-        // ---- x chunks: registers, branch-free (clamped address, then select)
-        const uint16_t *xrow[A_CH];
-        bool rlive[A_CH];
-#pragma unroll
-        for (int i = 0; i < A_CH; ++i) {
-            const int m = m0 + r0 + i * A_ROWS_PER_PASS;
-            rlive[i] = m < M;
-            xrow[i] = x + (int64_t)min(m, M - 1) * K;
-        }
-        u32x4 ra[2][A_CH], rg[2], rb[2];
-        auto load_a = [&](int kt, int set) {
-            kt = min(kt, nk - 1);
-            const int k = kt * BK + cc * 8;
-            const int kc = k < K ? k : 0;
-#pragma unroll
-            for (int i = 0; i < A_CH; ++i)
-                ra[set][i] = ldg128(xrow[i] + kc);
-            if constexpr (AFFINE) {
-                rg[set] = ldg128(gp + kc);
-                rb[set] = ldg128(bp + kc);
-            }
-        };
-
-        // issue order A(0) B(0) A(1) B(1) B(2): the steady-state step issues
-        // A(kt+2) then B(kt+3), and waits until 22 loads remain outstanding
-        load_a(0, 0);
-        issue_b(0, B0);
-        load_a(1, 1);
-        issue_b(1, B1);
-        issue_b(2, B2);
-
-        if constexpr (STATS == ST_FROM_Y) {
-            // statistics left by the statistics pass in this tile's own rows
-#pragma unroll
-            for (int i = 0; i < A_CH; ++i) {
-                const int m = min(m0 + r0 + i * A_ROWS_PER_PASS, M - 1);
-                const uint2 pk = *reinterpret_cast<const uint2 *>(y + (int64_t)m * N + n0);
-                rrs[i] = __builtin_bit_cast(float, pk.x);
-                rnmr[i] = __builtin_bit_cast(float, pk.y);
-            }
-        } else if constexpr (STATS == ST_PROLOGUE) {
-            {
-                // one wave per row, 4 rows at a time, reduced in fp32; staged
-                // through the second x stage (free until the first K step)
-                float *s_rs = reinterpret_cast<float *>(A1);
-                float *s_nmr = s_rs + BM;
-                const bool ln = norm == NORM_LAYERNORM;
-                const int nch = K / 8;
-                for (int rr = wave * (BM / NWAVE); rr < (wave + 1) * (BM / NWAVE); rr += 4) {
-                    float s1[4] = {0.f, 0.f, 0.f, 0.f}, s2[4] = {0.f, 0.f, 0.f, 0.f};
-                    uint32_t sh2[4];
-                    const uint16_t *rowp[4];
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int m = min(m0 + rr + q, M - 1);
-                        rowp[q] = x + (int64_t)m * K;
-                        const uint32_t s0 = ln ? (uint32_t)rowp[q][0] : 0u;
-                        sh2[q] = s0 | (s0 << 16);
-                    }
-                    for (int c = lane; c < nch; c += 64) {
-                        u32x4 v[4];
-#pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                            v[q] = ldg128(rowp[q] + c * 8);
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            if (ln)
-                                stats_chunk<DT, true>(v[q], sh2[q], s1[q], s2[q]);
-                            else
-                                stats_chunk<DT, false>(v[q], sh2[q], s1[q], s2[q]);
-                        }
-                    }
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const float a1 = wave_sum(s1[q]), a2 = wave_sum(s2[q]);
-                        float rs, nmr;
-                        finish_stats(a1, a2, bits_to_f<DT>((uint16_t)(sh2[q] & 0xffffu)), K, eps,
-                                     ln, rs, nmr);
-                        if (lane == 0) {
-                            s_rs[rr + q] = rs;
-                            s_nmr[rr + q] = nmr;
-                        }
-                    }
-                }
-                __syncthreads();
-#pragma unroll
-                for (int i = 0; i < A_CH; ++i) {
-                    rrs[i] = s_rs[r0 + i * A_ROWS_PER_PASS];
-                    rnmr[i] = s_nmr[r0 + i * A_ROWS_PER_PASS];
-                }
-                __syncthreads();
-            }
-        }
-
-        // normalized (or plain) x chunks of K step kt from register set `set`
-        // into stage buffer dst; rows past M and chunks past K become zero
-        auto store_a = [&](int kt, int set, u32x4 *dst) {
-            const bool kin = kt * BK + cc * 8 < K;
-            if constexpr (AFFINE) {
-                float g[8], b[8];
-                unpack8<DT>(rg[set], g);
-                unpack8<DT>(rb[set], b);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    g[e] = has_g ? g[e] : 1.0f;
-                    b[e] = has_b ? b[e] : 0.0f;
-                }
-#pragma unroll
-                for (int i = 0; i < A_CH; ++i) {
-                    const u32x4 v = normalize_chunk<DT>(ra[set][i], rrs[i], rnmr[i], g, b);
-                    dst[a_woff + i * A_ROWS_PER_PASS * CPR] =
-                        (kin && rlive[i]) ? v : u32x4{0u, 0u, 0u, 0u};
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < A_CH; ++i)
-                    dst[a_woff + i * A_ROWS_PER_PASS * CPR] =
-                        (kin && rlive[i]) ? ra[set][i] : u32x4{0u, 0u, 0u, 0u};
-            }
-        };
-
+        // complete them before the direct loads start: the compiler does not
+        // count those, so only an empty queue tells it these have landed
         wait_vmcnt<0>();
-        store_a(0, 0, A0);
-        if (k_tail && nk == 1)
-            fix_tail(B0);
-        if (k_tail && nk == 2)
-            fix_tail(B1);
-        if (k_tail && nk == 3)
-            fix_tail(B2);
-        lds_barrier();
-
-        floatx16 acc[FN][FM];
+    } else if constexpr (STATS == ST_PROLOGUE) {
+        // one wave per row, 4 rows at a time, reduced in fp32; exchanged
+        // through the third x stage (not loaded before the first K step)
+        float *s_rs = reinterpret_cast<float *>(A2);
+        float *s_nmr = s_rs + BM;
+        const bool ln = LN;
+        const int nch = K / 8;
+        for (int rr = wave * (BM / NWAVE); rr < (wave + 1) * (BM / NWAVE); rr += 4) {
+            float s1[4] = {0.f, 0.f, 0.f, 0.f}, s2[4] = {0.f, 0.f, 0.f, 0.f};
+            uint32_t sh2[4];
+            const uint16_t *rowp[4];
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
+            for (int q = 0; q < 4; ++q) {
+                const int m = min(m0 + rr + q, M - 1);
+                rowp[q] = x + (int64_t)m * K;
+                const uint32_t s0 = ln ? (uint32_t)rowp[q][0] : 0u;
+                sh2[q] = s0 | (s0 << 16);
+            }
+            for (int c = lane; c < nch; c += 64) {
+                u32x4 v[4];
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) acc[j][i][e] = 0.0f;
-
-        // Operand chunk of this lane for sub-step kk: rows 32 apart share the
-        // swizzle, so one offset per sub-step (plus compile-time row and
-        // stage offsets) addresses every fragment of every stage.
-        u32x4 wf[2][FN], xf[2][FM];
-        auto read_frags = [&](const u32x4 *Ac, const u32x4 *Bc, int kk, int buf) {
-            const int sw = swz(lrow, kk * 2 + lk);
-            const int aoff = (wm * WM + lrow) * CPR + sw;
-            const int boff = (wn * WN + lrow) * CPR + sw;
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-                wf[buf][j] = Bc[boff + j * 32 * CPR];
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-                xf[buf][i] = Ac[aoff + i * 32 * CPR];
-        };
-        auto mfmas = [&](int buf) {
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-#pragma unroll
-                for (int i = 0; i < FM; ++i)
-                    acc[j][i] = mfma32<DT>(wf[buf][j], xf[buf][i], acc[j][i]);
-        };
-        read_frags(A0, B0, 0, 0);
-
-        // One K step (stage indices static through the 4-way unroll):
-        //   issue x(kt+2) -> register set kt%2, W(kt+3) -> stage (kt+3)%4;
-        //   sub-steps 0..2 of kt, reading sub-step fragments one ahead;
-        //   wait until x(kt+1) and W(kt+1) arrived, write normalized x(kt+1);
-        //   barrier; fragments of sub-step 0 of kt+1; sub-step 3 of kt.
-        constexpr int kInflight = 2 * B_DMA + A_CH + (AFFINE ? 2 : 0);
-        auto step = [&](int kt, auto sc) {
-            constexpr int s = decltype(sc)::value;
-            using S1 = std::integral_constant<int, (s + 1) & 3>;
-            using S3 = std::integral_constant<int, (s + 3) & 3>;
-            const u32x4 *Ac = Ast(sc);
-            const u32x4 *Bc = Bst(sc);
-            load_a(kt + 2, s & 1);
-            issue_b(kt + 3, Bst(S3{}));
-            read_frags(Ac, Bc, 1, 1);
-            mfmas(0);
-            read_frags(Ac, Bc, 2, 0);
-            mfmas(1);
-            read_frags(Ac, Bc, 3, 1);
-            mfmas(0);
-            wait_vmcnt<kInflight>();
-            store_a(kt + 1, (s + 1) & 1, Ast(S1{}));
-            if (k_tail && kt + 1 == nk - 1)
-                fix_tail(Bst(S1{}));
-            lds_barrier();
-            read_frags(Ast(S1{}), Bst(S1{}), 0, 0);
-            mfmas(1);
-        };
-        for (int kt = 0; kt < nk; kt += 4) {
-            step(kt, I0{});
-            if (kt + 1 < nk)
-                step(kt + 1, I1{});
-            if (kt + 2 < nk)
-                step(kt + 2, I2{});
-            if (kt + 3 < nk)
-                step(kt + 3, I3{});
-        }
-        // drain the clamped loads issued past the last step before LDS reuse
-        wait_vmcnt<0>();
-        __syncthreads();
-
-        // ---- epilogue: bias + activation in registers, staged row-major in
-        // LDS (rows 0-63 in B0, 64-127 in B1; 16-byte chunks XOR-swizzled by
-        // row), then written with 128-bit stores
-        {
-            u32x4 *stg = wm ? B1 : B0;
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
+                for (int q = 0; q < 4; ++q)
+                    v[q] = ldg128(rowp[q] + c * 8);
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const int nl = wn * WN + j * 32 + q * 8 + lk * 4;
-                    float bv[4];
+                    if (ln)
+                        stats_chunk<DT, true>(v[q], sh2[q], s1[q], s2[q]);
+                    else
+                        stats_chunk<DT, false>(v[q], sh2[q], s1[q], s2[q]);
+                }
+            }
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int n = n0 + nl + r;
-                        bv[r] = (bias && n < N) ? bits_to_f<DT>(bias[n]) : 0.0f;
-                    }
-#pragma unroll
-                    for (int i = 0; i < FM; ++i) {
-                        const int ml = i * 32 + lrow;            // row within the half
-                        float v[4];
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            v[r] = apply_act(acc[j][i][q * 4 + r] + bv[r], act);
-                        const int chunk = (nl >> 3) ^ (ml & 31);
-                        uint32_t *dst = reinterpret_cast<uint32_t *>(&stg[ml * 32 + chunk]) + (lk * 2);
-                        dst[0] = pack2<DT>(v[0], v[1]);
-                        dst[1] = pack2<DT>(v[2], v[3]);
-                    }
+            for (int q = 0; q < 4; ++q) {
+                const float a1 = wave_sum(s1[q]), a2 = wave_sum(s2[q]);
+                float rs, nmr;
+                finish_stats(a1, a2, bits_to_f<DT>((uint16_t)(sh2[q] & 0xffffu)), K, eps, ln, rs,
+                             nmr);
+                if (lane == 0) {
+                    s_rs[rr + q] = rs;
+                    s_nmr[rr + q] = nmr;
                 }
             }
         }
         __syncthreads();
-        constexpr int ROWS_PER_PASS = THREADS / 32;
-#pragma unroll 4
-        for (int p = 0; p < BM / ROWS_PER_PASS; ++p) {
-            const int row = p * ROWS_PER_PASS + (tid >> 5), ch = tid & 31;
-            const int m = m0 + row, n = n0 + ch * 8;
-            const u32x4 *src = row < 64 ? B0 : B1;
-            const int rl = row & 63;
-            const u32x4 v = src[rl * 32 + (ch ^ (rl & 31))];
-            if (m >= M || n >= N)
-                continue;
-            uint16_t *dst = y + (int64_t)m * N + n;
-            if (vec_out && n + 8 <= N) {
-                *reinterpret_cast<u32x4 *>(dst) = v;
-            } else {
-                const int cnt = min(8, N - n);
-                for (int e = 0; e < cnt; ++e)
-                    dst[e] = (uint16_t)((v[e >> 1] >> ((e & 1) * 16)) & 0xffffu);
-            }
+#pragma unroll
+        for (int i = 0; i < A_DMA; ++i) {
+            const int row = i * A_IST + wave * 8 + (lane >> 3);
+            rrs[i] = s_rs[row];
+            rnmr[i] = s_nmr[row];
         }
         __syncthreads();
     }
+
+    // fp16 inputs: the affine step runs in packed fp16 arithmetic (two
+    // elements per instruction, no conversions): ((x - mu_hi) - mu_lo) * rs,
+    // then * gamma + beta; the mean is split into two fp16 parts so that
+    // x - mu stays accurate for rows with a large mean (statistics are fp32)
+    constexpr bool ln = LN;
+    half2_t mu_hi2[A_DMA], mu_lo2[A_DMA], rs2[A_DMA];
+    if constexpr (DT == DT_F16 && AFFINE) {
+#pragma unroll
+        for (int i = 0; i < A_DMA; ++i) {
+            const float mu = ln ? -rnmr[i] / rrs[i] : 0.0f;
+            const _Float16 hi = (_Float16)mu;
+            const _Float16 lo = (_Float16)(mu - (float)hi);
+            mu_hi2[i] = half2_t{hi, hi};
+            mu_lo2[i] = half2_t{lo, lo};
+            // 1/sigma beyond the fp16 range only arises for (near-)constant
+            // rows with a tiny eps, where x - mu is zero: clamp, not inf
+            const _Float16 r = (_Float16)fminf(rrs[i], 65504.0f);
+            rs2[i] = half2_t{r, r};
+        }
+    }
+
+    // x chunks of K step kt that this lane loaded: normalized + affine (fp32
+    // for bf16: x * rs + nmr, then * gamma + beta, one rounding; fp16: see
+    // above), written back in place; rows past M and chunks past K become
+    // zero. A lane's x rows are A_IST apart: one swizzle, so one logical
+    // chunk and one gamma / beta chunk for all of them. Split into the LDS
+    // reads and the arithmetic + write so that MFMAs can run in between.
+    struct NormRaw {
+        u32x4 v[A_DMA], g, b;
+    };
+    auto nrm_load = [&](const u32x4 *As, const u32x4 *Gs, NormRaw &r) {
+#pragma unroll
+        for (int i = 0; i < A_DMA; ++i)
+            r.v[i] = As[(i * A_IST + wave * 8) * CPR + lane];
+        r.g = r.b = u32x4{0u, 0u, 0u, 0u};
+        if constexpr (HG)
+            r.g = Gs[ach[0]];
+        if constexpr (HB)
+            r.b = Gs[64 + ach[0]];
+    };
+    auto nrm_store = [&](int kt, u32x4 *As, const NormRaw &r) {
+        const bool kin = kt * BK + ach[0] * 8 < K;
+        if constexpr (DT == DT_F16) {
+#pragma unroll
+            for (int i = 0; i < A_DMA; ++i) {
+                const bool live = alive[i] && kin;
+                u32x4 v = r.v[i];
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    // copy the elements first (bit_cast of a vector element
+                    // reference is miscompiled)
+                    const uint32_t xw = v[d], gd = r.g[d], bd = r.b[d];
+                    half2_t t = __builtin_bit_cast(half2_t, xw);
+                    if constexpr (ln)
+                        t = (t - mu_hi2[i]) - mu_lo2[i];
+                    t = t * rs2[i];
+                    if constexpr (HG && HB)
+                        t = t * __builtin_bit_cast(half2_t, gd) + __builtin_bit_cast(half2_t, bd);
+                    else if constexpr (HG)
+                        t = t * __builtin_bit_cast(half2_t, gd);
+                    else if constexpr (HB)
+                        t = t + __builtin_bit_cast(half2_t, bd);
+                    v[d] = __builtin_bit_cast(uint32_t, t);
+                }
+                As[(i * A_IST + wave * 8) * CPR + lane] = live ? v : u32x4{0u, 0u, 0u, 0u};
+            }
+        } else {
+            float g[8], bt[8];
+            if constexpr (HG)
+                unpack8<DT>(r.g, g);
+            if constexpr (HB)
+                unpack8<DT>(r.b, bt);
+#pragma unroll
+            for (int i = 0; i < A_DMA; ++i) {
+                const bool live = alive[i] && kin;
+                float f[8];
+                unpack8<DT>(r.v[i], f);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float v = fmaf(f[e], rrs[i], rnmr[i]);
+                    if constexpr (HG && HB)
+                        f[e] = fmaf(v, g[e], bt[e]);
+                    else if constexpr (HG)
+                        f[e] = v * g[e];
+                    else if constexpr (HB)
+                        f[e] = v + bt[e];
+                    else
+                        f[e] = v;
+                }
+                As[(i * A_IST + wave * 8) * CPR + lane] =
+                    live ? pack8<DT>(f) : u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+    };
+    auto normalize = [&](int kt, u32x4 *As, const u32x4 *Gs) {
+        NormRaw r;
+        nrm_load(As, Gs, r);
+        nrm_store(kt, As, r);
+    };
+    // without normalization only the chunks past K of the last step need
+    // zeroing (rows past M re-read row M - 1 and their outputs are dropped)
+    auto zero_tail_x = [&](u32x4 *As) {
+        if ((nk - 1) * BK + ach[0] * 8 >= K) {
+#pragma unroll
+            for (int i = 0; i < A_DMA; ++i)
+                As[(i * A_IST + wave * 8) * CPR + lane] = u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    auto fix_tail = [&](u32x4 *Bs) {
+#pragma unroll
+        for (int i = 0; i < B_DMA; ++i) {
+            const int row = wave * B_RPW + i * 8 + (lane >> 3);
+            if ((nk - 1) * BK + wch[i] * 8 >= K)
+                Bs[row * CPR + (lane & 7)] = u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+
+    // ---- prologue: K steps 0 and 1 in flight; step 0 normalized
+    issue_fence(x, gamma, beta);
+    issue(0, A0, B0, A0 + A_TILE);
+    issue(1, A1, B1, A1 + A_TILE);
+    issue_fence(x, gamma, beta);
+    wait_vmcnt<LPS>();                 // this wave's loads of step 0 have landed
+    issue_fence(x, gamma, beta);
+    if constexpr (AFFINE)
+        normalize(0, A0, A0 + A_TILE);
+    if (k_tail && nk == 1) {
+        if constexpr (!AFFINE)
+            zero_tail_x(A0);
+        fix_tail(B0);
+    }
+    lds_barrier();
+
+    floatx16 acc[FN][FM];
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[j][i][e] = 0.0f;
+
+    // Operand chunks of this lane for sub-step kk: rows 32 apart share the
+    // swizzle, so one offset per sub-step (plus compile-time row and stage
+    // offsets) addresses every fragment of every stage.
+    struct Frag {
+        u32x4 w[FN], a[FM];
+    };
+    auto rdfrag = [&](const u32x4 *Ac, const u32x4 *Bc, int kk, Frag &f) {
+        const int sw = swz(lrow, kk * 2 + lk);
+        const int aoff = (wm * WM + lrow) * CPR + sw;
+        const int boff = (wn * WN + lrow) * CPR + sw;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            f.w[j] = Bc[boff + j * 32 * CPR];
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+            f.a[i] = Ac[aoff + i * 32 * CPR];
+    };
+    auto mm = [&](const Frag &f, int j) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+            acc[j][i] = mfma32<DT>(f.w[j], f.a[i], acc[j][i]);
+    };
+    auto sb = [] { __builtin_amdgcn_sched_barrier(0); };
+
+    // One K step on stage kt % 3. The LPS direct loads of step kt + 2 go into
+    // the stage read in step kt - 1 (free since that step's barrier), one
+    // after each pair of MFMAs, x / gamma / beta first and W last, so that
+    // the load unit is fed while the matrix cores run. Fragments of the next
+    // sub-step are read before the MFMAs of the current one. Halfway, once
+    // the x / gamma / beta loads of step kt + 1 (issued first in step kt - 1)
+    // have landed -- younger are only that step's W loads and the four loads
+    // issued so far in this one -- the x chunks of step kt + 1 are normalized
+    // in place: read before sub-step 2, written back before sub-step 3. At
+    // the end this wave's loads of step kt + 1 have all landed (the LPS of
+    // step kt + 2 are the only younger ones); the barrier makes step kt + 1
+    // complete and normalized for every wave and frees stage kt % 3.
+    auto step = [&](int kt, auto sc) {
+        constexpr int s = decltype(sc)::value;
+        using S1 = std::integral_constant<int, s + 1>;
+        using S2 = std::integral_constant<int, s + 2>;
+        const u32x4 *Ac = Ast(sc);
+        const u32x4 *Bc = Bst(sc);
+        u32x4 *An = Ast(S2{}), *Bn = Bst(S2{}), *Gn = Gst(S2{});
+        const int kn = min(kt + 2, nk - 1);
+        const bool tl = KT && kn == nk - 1;
+        const char *wb = reinterpret_cast<const char *>(wtile) + (size_t)kn * (BK * 2);
+        const char *xb = reinterpret_cast<const char *>(xtile) + (size_t)kn * (BK * 2);
+        const char *gb = reinterpret_cast<const char *>(gamma) + (size_t)kn * (BK * 2);
+        const char *bb = reinterpret_cast<const char *>(beta) + (size_t)kn * (BK * 2);
+        auto slot = [&](auto dc) {
+            constexpr int d = decltype(dc)::value;
+            constexpr int NA = A_DMA + G_DMA;
+            if constexpr (d < A_DMA) {
+                dma16(xb, tl ? aoff_t[d] : aoff_g[d],
+                      lds_addr(&An[(d * A_IST + wave * 8) * CPR]));
+            } else if constexpr (d < NA) {
+                const uint32_t go_ = tl ? goff_t : goff;
+                if constexpr (HG && d == A_DMA)
+                    dma16(gb, go_, lds_addr(Gn));
+                else
+                    dma16(bb, go_, lds_addr(&Gn[64]));
+            } else if constexpr (d < LPS) {
+                constexpr int i = d - NA;
+                dma16(wb, tl ? woff_t[i] : woff[i],
+                      lds_addr(&Bn[(wave * B_RPW + i * 8) * CPR]));
+            }
+            sb();
+        };
+        using D0 = std::integral_constant<int, 0>;
+        using D1 = std::integral_constant<int, 1>;
+        using D2 = std::integral_constant<int, 2>;
+        using D3 = std::integral_constant<int, 3>;
+        using D4 = std::integral_constant<int, 4>;
+        using D5 = std::integral_constant<int, 5>;
+        using D6 = std::integral_constant<int, 6>;
+        using D7 = std::integral_constant<int, 7>;
+        static_assert(LPS <= 8, "eight load slots per K step");
+        Frag f0, f1;
+        NormRaw raw;
+        issue_fence(x, gamma, beta);
+        rdfrag(Ac, Bc, 0, f0);
+        sb();
+        // sub-step 0
+        rdfrag(Ac, Bc, 1, f1);
+        sb();
+        mm(f0, 0);
+        sb();
+        slot(D0{});
+        mm(f0, 1);
+        sb();
+        slot(D1{});
+        // sub-step 1
+        rdfrag(Ac, Bc, 2, f0);
+        sb();
+        mm(f1, 0);
+        sb();
+        slot(D2{});
+        mm(f1, 1);
+        sb();
+        slot(D3{});
+        if constexpr (AFFINE) {
+            wait_vmcnt<B_DMA + (LPS < 4 ? LPS : 4)>();
+            issue_fence(x, gamma, beta);
+            // (in the last step this normalizes a stage that is never read)
+            nrm_load(Ast(S1{}), Gst(S1{}), raw);
+            sb();
+        }
+        // sub-step 2
+        rdfrag(Ac, Bc, 3, f1);
+        sb();
+        mm(f0, 0);
+        if constexpr (AFFINE)
+            nrm_store(kt + 1, Ast(S1{}), raw);
+        sb();
+        slot(D4{});
+        mm(f0, 1);
+        sb();
+        slot(D5{});
+        // sub-step 3
+        mm(f1, 0);
+        sb();
+        slot(D6{});
+        mm(f1, 1);
+        sb();
+        slot(D7{});
+        wait_vmcnt<LPS>();
+        issue_fence(x, gamma, beta);
+        if (k_tail && kt + 1 == nk - 1) {
+            if constexpr (!AFFINE)
+                zero_tail_x(Ast(S1{}));
+            fix_tail(Bst(S1{}));
+        }
+        lds_barrier();
+    };
+    for (int kt = 0; kt < nk; kt += NSTAGE) {
+        step(kt, I0{});
+        if (kt + 1 < nk)
+            step(kt + 1, I1{});
+        if (kt + 2 < nk)
+            step(kt + 2, I2{});
+    }
+    // drain the clamped loads issued past the last step before LDS reuse
+    wait_vmcnt<0>();
+    __syncthreads();
+
+    // ---- epilogue: bias + activation in registers, staged row-major in
+    // LDS (rows 0-63 in B0, 64-127 in B1; 16-byte chunks XOR-swizzled by
+    // row), then written with 128-bit stores
+    {
+        u32x4 *stg = wm ? B1 : B0;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int nl = wn * WN + j * 32 + q * 8 + lk * 4;
+                float bv[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int n = n0 + nl + r;
+                    bv[r] = (bias && n < N) ? bits_to_f<DT>(bias[n]) : 0.0f;
+                }
+#pragma unroll
+                for (int i = 0; i < FM; ++i) {
+                    const int ml = i * 32 + lrow;            // row within the half
+                    float v[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        v[r] = apply_act(acc[j][i][q * 4 + r] + bv[r], act);
+                    const int chunk = (nl >> 3) ^ (ml & 31);
+                    uint32_t *dst = reinterpret_cast<uint32_t *>(&stg[ml * 32 + chunk]) + (lk * 2);
+                    dst[0] = pack2<DT>(v[0], v[1]);
+                    dst[1] = pack2<DT>(v[2], v[3]);
+                }
+            }
+        }
+    }
+    __syncthreads();
+    constexpr int ROWS_PER_PASS = THREADS / 32;
+#pragma unroll 4
+    for (int p = 0; p < BM / ROWS_PER_PASS; ++p) {
+        const int row = p * ROWS_PER_PASS + (tid >> 5), ch = tid & 31;
+        const int m = m0 + row, n = n0 + ch * 8;
+        const u32x4 *src = row < 64 ? B0 : B1;
+        const int rl = row & 63;
+        const u32x4 v = src[rl * 32 + (ch ^ (rl & 31))];
+        if (m >= M || n >= N)
+            continue;
+        uint16_t *dst = y + (int64_t)m * N + n;
+        if (vec_out && n + 8 <= N) {
+            *reinterpret_cast<u32x4 *>(dst) = v;
+        } else {
+            const int cnt = min(8, N - n);
+            for (int e = 0; e < cnt; ++e)
+                dst[e] = (uint16_t)((v[e >> 1] >> ((e & 1) * 16)) & 0xffffu);
+        }
+    }
 }
 
-template <int DT, int STATS>
-hipError_t launch_t(const GemmArgs &a, hipStream_t s)
+template <int DT, int STATS, int GB, bool KT, bool LN>
+hipError_t launch_k(const GemmArgs &a, hipStream_t s)
 {
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess)
@@ -557,23 +731,48 @@ hipError_t launch_t(const GemmArgs &a, hipStream_t s)
         if (e != hipSuccess)
             return e;
     }
-    hipLaunchKernelGGL((prefill_lds_kernel<DT, STATS>), dim3(mp.T), dim3(THREADS), 0, s,
+    hipLaunchKernelGGL((prefill_lds_kernel<DT, STATS, GB, KT, LN>), dim3(mp.T), dim3(THREADS), 0, s,
                        (const uint16_t *)a.x, (const uint16_t *)a.gamma, (const uint16_t *)a.beta,
                        (const uint16_t *)a.W, (const uint16_t *)a.bias, (uint16_t *)a.y, (int)a.M,
                        (int)a.N, (int)a.K, a.eps, a.norm, a.act, mp, vec_out);
     return hipGetLastError();
 }
 
+template <int DT, int STATS, int GB, bool LN>
+hipError_t launch_t(const GemmArgs &a, hipStream_t s)
+{
+    return a.K % BK ? launch_k<DT, STATS, GB, true, LN>(a, s)
+                    : launch_k<DT, STATS, GB, false, LN>(a, s);
+}
+
+template <int DT, int STATS, bool LN>
+hipError_t launch_gb(const GemmArgs &a, hipStream_t s)
+{
+    switch ((a.gamma ? 1 : 0) | (a.beta ? 2 : 0)) {
+    case 0: return launch_t<DT, STATS, 0, LN>(a, s);
+    case 1: return launch_t<DT, STATS, 1, LN>(a, s);
+    case 2: return launch_t<DT, STATS, 2, LN>(a, s);
+    default: return launch_t<DT, STATS, 3, LN>(a, s);
+    }
+}
+
+template <int DT, int STATS>
+hipError_t launch_norm(const GemmArgs &a, hipStream_t s)
+{
+    return a.norm == NORM_LAYERNORM ? launch_gb<DT, STATS, true>(a, s)
+                                    : launch_gb<DT, STATS, false>(a, s);
+}
+
 template <int DT>
 hipError_t launch_dt(const GemmArgs &a, hipStream_t s)
 {
     if (a.norm == NORM_NONE)
-        return launch_t<DT, ST_NONE>(a, s);
+        return launch_t<DT, ST_NONE, 0, false>(a, s);
     // The statistics pass needs 8 bytes of y in every tile's rows: every
     // tile (including the last, partial one) must have at least 4 columns
     // and the rows must be 8-byte aligned.
     const bool y_scratch = a.N % 8 == 0 && ((uintptr_t)a.y & 15u) == 0 && !stats_in_kernel();
-    return y_scratch ? launch_t<DT, ST_FROM_Y>(a, s) : launch_t<DT, ST_PROLOGUE>(a, s);
+    return y_scratch ? launch_norm<DT, ST_FROM_Y>(a, s) : launch_norm<DT, ST_PROLOGUE>(a, s);
 }
 
 }  // namespace
