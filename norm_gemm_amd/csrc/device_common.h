@@ -212,6 +212,29 @@ __device__ __forceinline__ void dma16(const void *sbase, uint32_t voff, uint32_t
                  : "memory", "m0");
 }
 
+// ------------------------------------------------ explicit register load
+// One 16-byte-per-lane load into registers (global_load_dwordx4, scalar base
+// + 32-bit vector offset) issued as inline asm: the compiler's own vmcnt
+// accounting does not see the direct loads, so for a load it can see it
+// would drain every direct load issued after it. The value arrives
+// asynchronously: it may only be read after wait_vmcnt_tied has taken it as
+// an in/out operand, which is where the compiler sees it defined.
+__device__ __forceinline__ u32x4 ldg16_async(const void *sbase, uint32_t voff)
+{
+    u32x4 r;
+    asm volatile("global_load_dwordx4 %0, %1, %2" : "=v"(r) : "v"(voff), "s"(sbase) : "memory");
+    return r;
+}
+
+// s_waitcnt vmcnt(N) that also hands the four registers through, so no read
+// of them can be placed before it
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_tied(u32x4 &a, u32x4 &b, u32x4 &c, u32x4 &d)
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%4)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) : "n"(N) : "memory");
+}
+
 // LDS byte address of a __shared__ object element, as a wave-uniform value
 __device__ __forceinline__ uint32_t lds_addr(const void *p)
 {

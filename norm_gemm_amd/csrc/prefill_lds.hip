@@ -49,11 +49,10 @@ constexpr int CPR = BK / 8;                      // 16-byte chunks per tile row
 constexpr int B_DMA = BN * CPR / THREADS;        // W direct loads per lane per K step (4)
 constexpr int A_TILE = BM * CPR, B_TILE = BN * CPR;   // in 16-byte chunks
 constexpr int NSTAGE = 3;                        // pipeline stages (loads 2 steps ahead)
-constexpr int G_CH = 128;                        // gamma / beta stage: 2 x 64 chunks
 constexpr int A_DMA = BM * CPR / THREADS;        // x direct loads per lane per K step (2)
 constexpr int A_RPW = BM / NWAVE;                // x rows loaded per wave per K step
 constexpr int A_IST = BM / A_DMA;                // rows between a lane's x rows (64)
-static_assert(NSTAGE * (A_TILE + B_TILE + G_CH) * 16 <= 160 * 1024, "LDS budget");
+static_assert(NSTAGE * (A_TILE + B_TILE) * 16 <= 160 * 1024, "LDS budget");
 static_assert(A_DMA * 8 == A_RPW && A_IST % 16 == 0, "x rows per wave; one swizzle per lane");
 constexpr int WM = 64, WN = 64;                  // wave tile (m x n)
 constexpr int WGM = BM / WM, WGN = BN / WN;      // wave grid (2 x 4)
@@ -183,14 +182,12 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
 {
     constexpr bool AFFINE = STATS != ST_NONE;
     constexpr bool HG = AFFINE && (GB & 1), HB = AFFINE && (GB & 2);
-    constexpr int G_DMA = (HG ? 1 : 0) + (HB ? 1 : 0);
-    constexpr int LPS = B_DMA + A_DMA + G_DMA;     // direct loads per lane per K step
-    // One LDS object per pipeline stage, so that the compiler can tell the
-    // stage being filled by direct loads from the stages being read.
-    // x stage s holds the x tile followed by the gamma / beta chunks of the
-    // same K step (one object per stage: at most six LDS objects are filled
-    // by direct loads, which the compiler still tracks one by one)
-    __shared__ u32x4 A0[A_TILE + G_CH], A1[A_TILE + G_CH], A2[A_TILE + G_CH];
+    // direct loads per lane per K step: W, plus x when it is not normalized
+    // (normalized x, gamma and beta come through registers)
+    constexpr int LPS = AFFINE ? B_DMA : B_DMA + A_DMA;
+    static_assert(A_DMA == 2, "two x chunks per lane");
+    // One LDS object per pipeline stage and operand
+    __shared__ u32x4 A0[A_TILE], A1[A_TILE], A2[A_TILE];
     __shared__ u32x4 B0[B_TILE], B1[B_TILE], B2[B_TILE];
     auto Ast = [&](auto sc) -> u32x4 * {
         constexpr int i = decltype(sc)::value % NSTAGE;
@@ -210,7 +207,6 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
         else
             return B2;
     };
-    auto Gst = [&](auto sc) -> u32x4 * { return Ast(sc) + A_TILE; };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
@@ -263,39 +259,21 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
         aoff_g[i] = (rb + ach[i] * 8) * 2u;
         aoff_t[i] = (rb + tail_chunk(ach[i]) * 8) * 2u;
     }
-    const uint32_t goff = (lane & 7) * 16u, goff_t = tail_chunk(lane & 7) * 16u;
-    auto issue = [&](int kt, u32x4 *As, u32x4 *Bs, u32x4 *Gs) {
+    // gamma / beta chunk of this lane's x chunks (tail: clamped in bounds)
+    const uint32_t goff = ach[0] * 16u, goff_t = tail_chunk(ach[0]) * 16u;
+    auto issue = [&](int kt, u32x4 *As, u32x4 *Bs) {
         kt = min(kt, nk - 1);
+        const bool tl = KT && kt == nk - 1;
         const char *wb = reinterpret_cast<const char *>(wtile) + (size_t)kt * (BK * 2);
         const char *xb = reinterpret_cast<const char *>(xtile) + (size_t)kt * (BK * 2);
-        const char *gb = reinterpret_cast<const char *>(gamma) + (size_t)kt * (BK * 2);
-        const char *bb = reinterpret_cast<const char *>(beta) + (size_t)kt * (BK * 2);
-        // direct loads as explicit asm (see dma16): the compiler inserts no
-        // waits of its own in the K loop; the step's vmcnt wait and barrier
-        // order everything
-        // x, gamma, beta, then W: the order of the load slots of the K loop
-        auto go = [&](const uint32_t *wo, const uint32_t *ao, uint32_t go_) {
+        if constexpr (!AFFINE) {
 #pragma unroll
             for (int i = 0; i < A_DMA; ++i)
-                dma16(xb, ao[i], lds_addr(&As[(i * A_IST + wave * 8) * CPR]));
-            // gamma chunks 0-7 at positions 0-7 (lanes 8-63 repeat them), beta
-            // chunks at 64 + 0-7
-            if constexpr (HG)
-                dma16(gb, go_, lds_addr(Gs));
-            if constexpr (HB)
-                dma16(bb, go_, lds_addr(&Gs[64]));
-#pragma unroll
-            for (int i = 0; i < B_DMA; ++i)
-                dma16(wb, wo[i], lds_addr(&Bs[(wave * B_RPW + i * 8) * CPR]));
-        };
-        if constexpr (!KT) {
-            go(woff, aoff_g, goff);
-        } else {
-            if (kt < nk - 1)
-                go(woff, aoff_g, goff);
-            else
-                go(woff_t, aoff_t, goff_t);
+                dma16(xb, tl ? aoff_t[i] : aoff_g[i], lds_addr(&As[(i * A_IST + wave * 8) * CPR]));
         }
+#pragma unroll
+        for (int i = 0; i < B_DMA; ++i)
+            dma16(wb, tl ? woff_t[i] : woff[i], lds_addr(&Bs[(wave * B_RPW + i * 8) * CPR]));
     };
 
     // (rs, nmr) of the rows of this lane's x chunks
@@ -400,15 +378,23 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
     struct NormRaw {
         u32x4 v[A_DMA], g, b;
     };
-    auto nrm_load = [&](const u32x4 *As, const u32x4 *Gs, NormRaw &r) {
+    // x / gamma / beta chunks of K step kt into registers (asynchronous: see
+    // ldg16_async; NXL loads, completed by wait_vmcnt_tied)
+    constexpr int NXL = A_DMA + (HG ? 1 : 0) + (HB ? 1 : 0);
+    auto load_raw = [&](int kt, NormRaw &r) {
+        kt = min(kt, nk - 1);
+        const bool tl = KT && kt == nk - 1;
+        const char *xb = reinterpret_cast<const char *>(xtile) + (size_t)kt * (BK * 2);
+        const char *gb = reinterpret_cast<const char *>(gamma) + (size_t)kt * (BK * 2);
+        const char *bb = reinterpret_cast<const char *>(beta) + (size_t)kt * (BK * 2);
 #pragma unroll
         for (int i = 0; i < A_DMA; ++i)
-            r.v[i] = As[(i * A_IST + wave * 8) * CPR + lane];
+            r.v[i] = ldg16_async(xb, tl ? aoff_t[i] : aoff_g[i]);
         r.g = r.b = u32x4{0u, 0u, 0u, 0u};
         if constexpr (HG)
-            r.g = Gs[ach[0]];
+            r.g = ldg16_async(gb, tl ? goff_t : goff);
         if constexpr (HB)
-            r.b = Gs[64 + ach[0]];
+            r.b = ldg16_async(bb, tl ? goff_t : goff);
     };
     auto nrm_store = [&](int kt, u32x4 *As, const NormRaw &r) {
         const bool kin = kt * BK + ach[0] * 8 < K;
@@ -464,11 +450,6 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
             }
         }
     };
-    auto normalize = [&](int kt, u32x4 *As, const u32x4 *Gs) {
-        NormRaw r;
-        nrm_load(As, Gs, r);
-        nrm_store(kt, As, r);
-    };
     // without normalization only the chunks past K of the last step need
     // zeroing (rows past M re-read row M - 1 and their outputs are dropped)
     auto zero_tail_x = [&](u32x4 *As) {
@@ -489,13 +470,20 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
 
     // ---- prologue: K steps 0 and 1 in flight; step 0 normalized
     issue_fence(x, gamma, beta);
-    issue(0, A0, B0, A0 + A_TILE);
-    issue(1, A1, B1, A1 + A_TILE);
+    if constexpr (AFFINE) {
+        NormRaw r0;
+        load_raw(0, r0);
+        issue(0, A0, B0);
+        issue(1, A1, B1);
+        wait_vmcnt_tied<2 * LPS>(r0.v[0], r0.v[1], r0.g, r0.b);
+        nrm_store(0, A0, r0);
+    } else {
+        issue(0, A0, B0);
+        issue(1, A1, B1);
+    }
     issue_fence(x, gamma, beta);
     wait_vmcnt<LPS>();                 // this wave's loads of step 0 have landed
     issue_fence(x, gamma, beta);
-    if constexpr (AFFINE)
-        normalize(0, A0, A0 + A_TILE);
     if (k_tail && nk == 1) {
         if constexpr (!AFFINE)
             zero_tail_x(A0);
@@ -535,43 +523,39 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
     };
     auto sb = [] { __builtin_amdgcn_sched_barrier(0); };
 
-    // One K step on stage kt % 3. The LPS direct loads of step kt + 2 go into
-    // the stage read in step kt - 1 (free since that step's barrier), one
-    // after each pair of MFMAs, x / gamma / beta first and W last, so that
-    // the load unit is fed while the matrix cores run. Fragments of the next
-    // sub-step are read before the MFMAs of the current one. Halfway, once
-    // the x / gamma / beta loads of step kt + 1 (issued first in step kt - 1)
-    // have landed -- younger are only that step's W loads and the four loads
-    // issued so far in this one -- the x chunks of step kt + 1 are normalized
-    // in place: read before sub-step 2, written back before sub-step 3. At
-    // the end this wave's loads of step kt + 1 have all landed (the LPS of
+    // One K step on stage kt % 3. The direct loads of step kt + 2 go into the
+    // stage read in step kt - 1 (free since that step's barrier), one after
+    // a pair of MFMAs, so that the load unit is fed while the matrix cores
+    // run; fragments of the next sub-step are read before the MFMAs of the
+    // current one.
+    //   normalized x: the x / gamma / beta chunks of step kt + 1 are loaded
+    //   into registers at the start of the step; in sub-step 3 (younger are
+    //   only the three W loads issued since) they are normalized and written
+    //   once into stage (kt + 1) % 3, last read in step kt - 2. W goes one
+    //   load per sub-step.
+    //   plain x: x and W of step kt + 2 both go direct, in the first six
+    //   slots.
+    // At the end this wave's loads of step kt + 1 have landed (the LPS of
     // step kt + 2 are the only younger ones); the barrier makes step kt + 1
-    // complete and normalized for every wave and frees stage kt % 3.
+    // complete for every wave and frees stage kt % 3.
     auto step = [&](int kt, auto sc) {
         constexpr int s = decltype(sc)::value;
         using S1 = std::integral_constant<int, s + 1>;
         using S2 = std::integral_constant<int, s + 2>;
         const u32x4 *Ac = Ast(sc);
         const u32x4 *Bc = Bst(sc);
-        u32x4 *An = Ast(S2{}), *Bn = Bst(S2{}), *Gn = Gst(S2{});
+        u32x4 *An = Ast(S2{}), *Bn = Bst(S2{});
         const int kn = min(kt + 2, nk - 1);
         const bool tl = KT && kn == nk - 1;
         const char *wb = reinterpret_cast<const char *>(wtile) + (size_t)kn * (BK * 2);
         const char *xb = reinterpret_cast<const char *>(xtile) + (size_t)kn * (BK * 2);
-        const char *gb = reinterpret_cast<const char *>(gamma) + (size_t)kn * (BK * 2);
-        const char *bb = reinterpret_cast<const char *>(beta) + (size_t)kn * (BK * 2);
+        // load slot d: x chunks first when x goes direct, then W
         auto slot = [&](auto dc) {
             constexpr int d = decltype(dc)::value;
-            constexpr int NA = A_DMA + G_DMA;
-            if constexpr (d < A_DMA) {
+            constexpr int NA = AFFINE ? 0 : A_DMA;
+            if constexpr (d < NA) {
                 dma16(xb, tl ? aoff_t[d] : aoff_g[d],
                       lds_addr(&An[(d * A_IST + wave * 8) * CPR]));
-            } else if constexpr (d < NA) {
-                const uint32_t go_ = tl ? goff_t : goff;
-                if constexpr (HG && d == A_DMA)
-                    dma16(gb, go_, lds_addr(Gn));
-                else
-                    dma16(bb, go_, lds_addr(&Gn[64]));
             } else if constexpr (d < LPS) {
                 constexpr int i = d - NA;
                 dma16(wb, tl ? woff_t[i] : woff[i],
@@ -585,57 +569,77 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
         using D3 = std::integral_constant<int, 3>;
         using D4 = std::integral_constant<int, 4>;
         using D5 = std::integral_constant<int, 5>;
-        using D6 = std::integral_constant<int, 6>;
-        using D7 = std::integral_constant<int, 7>;
-        static_assert(LPS <= 8, "eight load slots per K step");
         Frag f0, f1;
-        NormRaw raw;
         issue_fence(x, gamma, beta);
-        rdfrag(Ac, Bc, 0, f0);
-        sb();
-        // sub-step 0
-        rdfrag(Ac, Bc, 1, f1);
-        sb();
-        mm(f0, 0);
-        sb();
-        slot(D0{});
-        mm(f0, 1);
-        sb();
-        slot(D1{});
-        // sub-step 1
-        rdfrag(Ac, Bc, 2, f0);
-        sb();
-        mm(f1, 0);
-        sb();
-        slot(D2{});
-        mm(f1, 1);
-        sb();
-        slot(D3{});
         if constexpr (AFFINE) {
-            wait_vmcnt<B_DMA + (LPS < 4 ? LPS : 4)>();
-            issue_fence(x, gamma, beta);
+            static_assert(LPS == 4, "one W load per sub-step");
+            NormRaw raw;
+            load_raw(kt + 1, raw);
+            sb();
+            rdfrag(Ac, Bc, 0, f0);
+            sb();
+            rdfrag(Ac, Bc, 1, f1);
+            sb();
+            mm(f0, 0);
+            sb();
+            slot(D0{});
+            mm(f0, 1);
+            sb();
+            rdfrag(Ac, Bc, 2, f0);
+            sb();
+            mm(f1, 0);
+            sb();
+            slot(D1{});
+            mm(f1, 1);
+            sb();
+            rdfrag(Ac, Bc, 3, f1);
+            sb();
+            mm(f0, 0);
+            sb();
+            slot(D2{});
+            mm(f0, 1);
+            sb();
+            wait_vmcnt_tied<3>(raw.v[0], raw.v[1], raw.g, raw.b);
+            mm(f1, 0);
             // (in the last step this normalizes a stage that is never read)
-            nrm_load(Ast(S1{}), Gst(S1{}), raw);
+            nrm_store(kt + 1, Ast(S1{}), raw);
+            sb();
+            slot(D3{});
+            mm(f1, 1);
+            sb();
+        } else {
+            static_assert(LPS == 6, "six direct loads per K step");
+            rdfrag(Ac, Bc, 0, f0);
+            sb();
+            rdfrag(Ac, Bc, 1, f1);
+            sb();
+            mm(f0, 0);
+            sb();
+            slot(D0{});
+            mm(f0, 1);
+            sb();
+            slot(D1{});
+            rdfrag(Ac, Bc, 2, f0);
+            sb();
+            mm(f1, 0);
+            sb();
+            slot(D2{});
+            mm(f1, 1);
+            sb();
+            slot(D3{});
+            rdfrag(Ac, Bc, 3, f1);
+            sb();
+            mm(f0, 0);
+            sb();
+            slot(D4{});
+            mm(f0, 1);
+            sb();
+            slot(D5{});
+            mm(f1, 0);
+            sb();
+            mm(f1, 1);
             sb();
         }
-        // sub-step 2
-        rdfrag(Ac, Bc, 3, f1);
-        sb();
-        mm(f0, 0);
-        if constexpr (AFFINE)
-            nrm_store(kt + 1, Ast(S1{}), raw);
-        sb();
-        slot(D4{});
-        mm(f0, 1);
-        sb();
-        slot(D5{});
-        // sub-step 3
-        mm(f1, 0);
-        sb();
-        slot(D6{});
-        mm(f1, 1);
-        sb();
-        slot(D7{});
         wait_vmcnt<LPS>();
         issue_fence(x, gamma, beta);
         if (k_tail && kt + 1 == nk - 1) {
