@@ -62,9 +62,19 @@ __device__ __forceinline__ void static_for(F &&f)
     }
 }
 
-// MB = number of 16-column blocks of M (1 for M <= 16, 2 for M <= 32);
-// NBK = 16-row blocks of W per workgroup (2..8).
-template <int DT, bool AFFINE, int MB, int NBK>
+// Normalization modes of the kernel.
+enum {
+    DM_NONE = 0,      // x as given
+    DM_STATS = 1,     // LayerNorm / RMSNorm: row statistics first, then
+                      // (x - mu) * rs * gamma + beta in registers
+    DM_RMS_LATE = 2,  // RMSNorm without beta, bf16: x * gamma into the MFMA,
+                      // each row's sum of x^2 on the matrix cores, rs applied
+                      // per output row at the end
+};
+
+// DM = normalization mode; MB = number of 16-column blocks of M (1 for
+// M <= 16, 2 for M <= 32); NBK = 16-row blocks of W per workgroup (2..8).
+template <int DT, int DM, int MB, int NBK>
 __global__ __launch_bounds__(64 * kNW) void decode_lds_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ gamma,
     const uint16_t *__restrict__ beta, const uint16_t *__restrict__ W,
@@ -72,12 +82,17 @@ __global__ __launch_bounds__(64 * kNW) void decode_lds_kernel(
     float eps, int norm, int act)
 {
     static_assert(NBK >= 2 && NBK <= kNBMax, "2..8 row blocks per workgroup");
+    constexpr bool AFFINE = DM == DM_STATS;
+    constexpr bool LATE = DM == DM_RMS_LATE;
     constexpr int D = NBK - 1;                          // blocks in flight per wave
-    constexpr int XL = 2 * MB + (AFFINE ? 4 : 0);       // loads per x group
+    // loads per x group: x chunks, plus gamma and beta (statistics mode) or
+    // gamma (late RMS scaling)
+    constexpr int XL = 2 * MB + (AFFINE ? 4 : LATE ? 2 : 0);
     __shared__ u32x4 L0[kNW][kBlockChunks], L1[kNW][kBlockChunks], L2[kNW][kBlockChunks],
         L3[kNW][kBlockChunks], L4[kNW][kBlockChunks], L5[kNW][kBlockChunks],
         L6[kNW][kBlockChunks], L7[kNW][kBlockChunks];
     __shared__ float s_rs[32], s_mu[32];
+    __shared__ float s_ss[kNW][32];     // late RMS: per-wave sums of x^2 per row
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -137,10 +152,10 @@ __global__ __launch_bounds__(64 * kNW) void decode_lds_kernel(
         for (int s2 = 0; s2 < 2; ++s2) {
             const int k = kb * 64 + (4 * s2 + lg) * 8;
             const int kc = k < K ? k : 0;
-            if constexpr (AFFINE) {
+            if constexpr (AFFINE || LATE)
                 gr[set][s2] = ldg128(gp + kc);
+            if constexpr (AFFINE)
                 br[set][s2] = ldg128(bp + kc);
-            }
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
                 xr[set][mb][s2] = ldg128(x + (int64_t)min(mb * 16 + lr, M - 1) * K + kc);
@@ -179,12 +194,43 @@ __global__ __launch_bounds__(64 * kNW) void decode_lds_kernel(
         }
     }
 
-    // normalized B operands of k-block kb from register set SET
+    // B operands of k-block kb from register set SET: normalized (statistics
+    // mode), times gamma with the sums of x^2 taken on the way (late RMS), or
+    // x itself
+    floatx4 accss[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+        accss[mb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
     auto x_frags = [&](auto SET, int kb, u32x4 (&xf)[MB][2]) {
         constexpr int set = decltype(SET)::value;
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
             const bool kin = kb * 64 + (4 * s2 + lg) * 8 < K;
+            if constexpr (LATE) {
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) {
+                    const bool live = kin && mb * 16 + lr < M;
+                    // x masked once. The A and B operand layouts of the
+                    // 16x16x32 MFMA coincide (lane l: row l % 16, k-group
+                    // l / 16), so x times itself accumulates
+                    // C[i][j] = sum_k x_ik x_jk, whose diagonal holds each
+                    // row's sum of squares (bf16 products are exact in fp32)
+                    const u32x4 xz = live ? xr[set][mb][s2] : u32x4{0u, 0u, 0u, 0u};
+                    accss[mb] = mfma16<DT>(xz, xz, accss[mb]);
+                    if (gamma) {
+                        float f[8], g[8];
+                        unpack8<DT>(xz, f);
+                        unpack8<DT>(gr[set][s2], g);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            f[e] *= g[e];
+                        xf[mb][s2] = pack8<DT>(f);
+                    } else {
+                        xf[mb][s2] = xz;
+                    }
+                }
+                continue;
+            }
             float g[8], bt[8];
             if constexpr (AFFINE) {
                 unpack8<DT>(gr[set][s2], g);
@@ -286,7 +332,18 @@ __global__ __launch_bounds__(64 * kNW) void decode_lds_kernel(
     wait_vmcnt<0>();
 
     // Partials: wave w writes its row block nb into its own slot nb as
-    // float [16 n][16 MB m] (1 KB per 16 m, fits the 2 KB slot).
+    // float [16 n][16 MB m] (1 KB per 16 m, fits the 2 KB slot); late RMS:
+    // the wave's sum of x^2 per row (diagonal element i of a 16x16 result
+    // sits in lane i + 16 (i / 4), accumulator register i % 4).
+    if constexpr (LATE) {
+        if (lg == (lr >> 2)) {
+            const int r = lr & 3;
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+                s_ss[wave][mb * 16 + lr] = r == 0 ? accss[mb][0] : r == 1 ? accss[mb][1]
+                                         : r == 2 ? accss[mb][2] : accss[mb][3];
+        }
+    }
     static_for<0, NBK>([&](auto NB) {
         constexpr int nb = decltype(NB)::value;
         float *p = reinterpret_cast<float *>(slot(NB, wave));
@@ -309,6 +366,13 @@ __global__ __launch_bounds__(64 * kNW) void decode_lds_kernel(
 #pragma unroll
             for (int w = 0; w < kNW; ++w)
                 v += reinterpret_cast<const float *>(slot(NB, w))[nr * (16 * MB) + m];
+            if constexpr (LATE) {
+                float q = 0.0f;
+#pragma unroll
+                for (int w = 0; w < kNW; ++w)
+                    q += s_ss[w][m];
+                v *= rsqrtf(q / (float)K + eps);
+            }
             if (n < N) {
                 if (bias)
                     v += bits_to_f<DT>(bias[n]);
@@ -318,7 +382,7 @@ __global__ __launch_bounds__(64 * kNW) void decode_lds_kernel(
     });
 }
 
-template <int DT, bool AFFINE, int NBK>
+template <int DT, int DM, int NBK>
 hipError_t launch_t(const GemmArgs &a, int grid, hipStream_t s)
 {
 #define NG_DECODE_ARGS                                                                       \
@@ -326,26 +390,26 @@ hipError_t launch_t(const GemmArgs &a, int grid, hipStream_t s)
         (const uint16_t *)a.W, (const uint16_t *)a.bias, (uint16_t *)a.y, (int)a.M, (int)a.N, \
         (int)a.K, a.eps, a.norm, a.act
     if (a.M <= 16)
-        hipLaunchKernelGGL((decode_lds_kernel<DT, AFFINE, 1, NBK>), dim3(grid), dim3(64 * kNW), 0,
-                           s, NG_DECODE_ARGS);
+        hipLaunchKernelGGL((decode_lds_kernel<DT, DM, 1, NBK>), dim3(grid), dim3(64 * kNW), 0, s,
+                           NG_DECODE_ARGS);
     else
-        hipLaunchKernelGGL((decode_lds_kernel<DT, AFFINE, 2, NBK>), dim3(grid), dim3(64 * kNW), 0,
-                           s, NG_DECODE_ARGS);
+        hipLaunchKernelGGL((decode_lds_kernel<DT, DM, 2, NBK>), dim3(grid), dim3(64 * kNW), 0, s,
+                           NG_DECODE_ARGS);
 #undef NG_DECODE_ARGS
     return hipGetLastError();
 }
 
-template <int DT, bool AFFINE>
+template <int DT, int DM>
 hipError_t launch_nbk(const GemmArgs &a, int nbk, int grid, hipStream_t s)
 {
     switch (nbk) {
-    case 2: return launch_t<DT, AFFINE, 2>(a, grid, s);
-    case 3: return launch_t<DT, AFFINE, 3>(a, grid, s);
-    case 4: return launch_t<DT, AFFINE, 4>(a, grid, s);
-    case 5: return launch_t<DT, AFFINE, 5>(a, grid, s);
-    case 6: return launch_t<DT, AFFINE, 6>(a, grid, s);
-    case 7: return launch_t<DT, AFFINE, 7>(a, grid, s);
-    default: return launch_t<DT, AFFINE, 8>(a, grid, s);
+    case 2: return launch_t<DT, DM, 2>(a, grid, s);
+    case 3: return launch_t<DT, DM, 3>(a, grid, s);
+    case 4: return launch_t<DT, DM, 4>(a, grid, s);
+    case 5: return launch_t<DT, DM, 5>(a, grid, s);
+    case 6: return launch_t<DT, DM, 6>(a, grid, s);
+    case 7: return launch_t<DT, DM, 7>(a, grid, s);
+    default: return launch_t<DT, DM, 8>(a, grid, s);
     }
 }
 
@@ -364,12 +428,16 @@ hipError_t launch_decode_lds(const GemmArgs &a, hipStream_t s)
     int64_t nbk = (blocks + cus - 1) / cus;
     nbk = nbk < 2 ? 2 : (nbk > kNBMax ? kNBMax : nbk);
     const int grid = (int)((blocks + nbk - 1) / nbk);
-    const bool affine = a.norm != NORM_NONE;
+    if (a.norm == NORM_NONE)
+        return a.dtype == DT_F16 ? launch_nbk<DT_F16, DM_NONE>(a, (int)nbk, grid, s)
+                                 : launch_nbk<DT_BF16, DM_NONE>(a, (int)nbk, grid, s);
     if (a.dtype == DT_F16)
-        return affine ? launch_nbk<DT_F16, true>(a, (int)nbk, grid, s)
-                      : launch_nbk<DT_F16, false>(a, (int)nbk, grid, s);
-    return affine ? launch_nbk<DT_BF16, true>(a, (int)nbk, grid, s)
-                  : launch_nbk<DT_BF16, false>(a, (int)nbk, grid, s);
+        return launch_nbk<DT_F16, DM_STATS>(a, (int)nbk, grid, s);
+    // bf16 RMSNorm without beta: scale after the product (x * gamma stays in
+    // bf16 range, no statistics pass before the W stream)
+    if (a.norm == NORM_RMSNORM && !a.beta)
+        return launch_nbk<DT_BF16, DM_RMS_LATE>(a, (int)nbk, grid, s);
+    return launch_nbk<DT_BF16, DM_STATS>(a, (int)nbk, grid, s);
 }
 
 }  // namespace ng

@@ -99,6 +99,27 @@ def test_decode_slab_heights(M, N, K, norm, act, dtype, bias):
     check_full(case)
 
 
+# bf16 RMSNorm without beta on the 16-row-slab kernel (M 17..32) scales after
+# the product, with each row's sum of squares taken on the matrix cores:
+# ragged K, rows past 8192, idle waves, N below one slab, with and without
+# gamma, with SiLU and bias after the scaling
+DECODE_LATE_RMS_SHAPES = [
+    (17, 9000, 200, True, ACT0, True),
+    (24, 13000, 1096, False, SILU, False),
+    (32, 21000, 520, True, SILU, True),
+    (32, 4100, 16384, True, ACT0, False),
+    (20, 17, 1024, False, ACT0, True),
+]
+
+
+@pytest.mark.parametrize("M,N,K,gamma,act,bias", DECODE_LATE_RMS_SHAPES)
+def test_decode_late_rms_scaling(M, N, K, gamma, act, bias):
+    case = synth.make_norm_gemm(f"decode_late_rms_{M}x{N}x{K}", M, K, N, dtype=BF16, norm=RMS,
+                                act=act, gamma=gamma, beta=False, bias=bias, eps=1e-6,
+                                seed=M * 3 + N + K)
+    check_full(case)
+
+
 @pytest.mark.parametrize("M", [5, 100])
 @pytest.mark.parametrize("gamma,beta,bias", [(False, False, False), (True, False, True),
                                              (False, True, False)])
