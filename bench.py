@@ -143,22 +143,29 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+    # Whole-job throughput: exactly K steps back to back between two events
+    # (per-step events would add their own gaps to the total).
     t_all0, t_all1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_all0.record(stream)
     for i in range(args.steps):
-        ev[i][0].record(stream)
         step(i)
-        ev[i][1].record(stream)
     t_all1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = t_all0.elapsed_time(t_all1)
-    per_launch = np.array([a.elapsed_time(b) for a, b in ev])
     ms_per_step = total_ms / args.steps
+    # Per-launch durations for the roofline: a second pass of K steps, each
+    # bracketed by events on the stream the kernels run on.
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    per_launch = np.array([a.elapsed_time(b) for a, b in ev])
     avg_launch_ms = float(per_launch.mean())
 
     decode = case.M <= 32

@@ -96,7 +96,7 @@ __global__ __launch_bounds__(64 * kNW) void decode_lds_kernel(
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 15, lg = lane >> 4;
     const int n0 = blockIdx.x * (NBK * 16);
 
@@ -121,12 +121,17 @@ __global__ __launch_bounds__(64 * kNW) void decode_lds_kernel(
 
     // Direct loads of block (kb, NB) into slot NB: load h (0/1) puts row
     // 8h + lane/8 at chunk position lane%8, holding logical chunk
-    // dswz(row, lane%8). A k-block past this wave's range re-loads the last
-    // one (its slot is never read again).
+    // dswz(row, lane%8). A block past this wave's range keeps the load
+    // count uniform: it re-reads the wave's most recently loaded block (the
+    // last row block of its last k-block, still in L2) into a slot that is
+    // never read again.
     const int drow0 = lane >> 3;
     auto issue_block = [&](auto NB, int kb) {
-        constexpr int nb = decltype(NB)::value;
-        kb = min(kb, kb1 - 1);
+        int nb = decltype(NB)::value;
+        if (kb >= kb1) {
+            kb = kb1 - 1;
+            nb = NBK - 1;
+        }
         u32x4 *dst = slot(NB, wave);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {

@@ -94,7 +94,7 @@ __global__ __launch_bounds__(64 * kNW) void decode_wide_kernel(
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 15, lg = lane >> 4;
     // slab of W rows; the last workgroup's slab is moved back to end at N
     // (N >= 16 NBK), overlapping its neighbour, which computes the shared
@@ -119,17 +119,23 @@ __global__ __launch_bounds__(64 * kNW) void decode_wide_kernel(
     // 2q + lane/32 at chunk position lane%32, holding logical chunk
     // (lane%32) ^ row = ((lane%32) ^ (lane/32)) ^ 2q. The row offset is
     // uniform except for lane/32, so the per-lane address part is one small
-    // term. A k-block past this wave's range re-loads the last one into the
-    // slot that was just consumed (never read again). (Direct loads through
-    // a buffer descriptor would need fewer registers, but the compiler then
-    // loses which LDS slot each load writes and waits for all of them
-    // before every LDS read.)
+    // term. A block past this wave's range keeps the load count (and so the
+    // waits) uniform: it re-reads the wave's most recently loaded block (the
+    // last row block of its last k-block, still in L2) into the slot that
+    // was just consumed (never read again). (Direct loads through a buffer
+    // descriptor would need fewer registers, but the compiler then loses
+    // which LDS slot each load writes and waits for all of them before
+    // every LDS read.)
     const int dpos = lane & 31;
     const int drow = lane >> 5;
     const int lchunk = dpos ^ drow;
     const int lrowoff = drow * K;
     auto issue_block = [&](auto SL, int kb, int nb) {
-        kb = max(min(kb, kb1 - 1), 0);
+        if (kb >= kb1) {
+            kb = kb1 - 1;
+            nb = NBK - 1;
+        }
+        kb = max(kb, 0);
         u32x4 *dst = slot(SL, wave);
         const uint16_t *wb = W + (int64_t)(n0 + nb * 16) * K;
 #pragma unroll
