@@ -42,7 +42,7 @@ class NormGemmError(RuntimeError):
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIBRARY_PATH):
-        raise ImportError(f"{LIBRARY_PATH} is not built; run `python -m norm_gemm_amd.build`")
+        raise ImportError(f"{LIBRARY_PATH} is not built; run `python norm_gemm_amd/build.py` from the repository root")
     L = ctypes.CDLL(LIBRARY_PATH)
     vp, i64, f32, ci, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int, ctypes.c_size_t
     L.fused_norm_gemm.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, f32, ci, ci, ci, vp]

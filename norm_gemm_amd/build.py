@@ -1,6 +1,6 @@
 """Build the gfx950 library ``libnormgemm.so`` in-tree with hipcc.
 
-Usage: ``python -m norm_gemm_amd.build`` (also called by the repository's
+Usage: ``python norm_gemm_amd/build.py`` (also called by the repository's
 build entry point). Every HIP source is compiled for gfx950 only; the C
 validation layer is compiled as plain host C. Objects go to
 ``norm_gemm_amd/_build/``; the library is written next to this file.

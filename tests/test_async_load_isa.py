@@ -15,7 +15,13 @@ import subprocess
 
 import pytest
 
-from norm_gemm_amd import build as nb
+import importlib.util
+
+_spec = importlib.util.spec_from_file_location(
+    "_norm_gemm_amd_build",
+    os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "norm_gemm_amd", "build.py"))
+nb = importlib.util.module_from_spec(_spec)
+_spec.loader.exec_module(nb)
 
 HIPCC = nb.HIPCC
 
