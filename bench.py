@@ -3,6 +3,9 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
+Defaults: K = 100 timed steps after W = 400 untimed ones (the clock reaches
+its steady state under load only after tens of milliseconds).
+
 A step is one call of the hot path on one batch of synthetic input that is
 already resident in device memory. The default workload is LayerNorm +
 Linear + bias on x[1024, 8192] (batch 8 x seq 128) and W[8192, 8192] in fp16.
@@ -90,8 +93,10 @@ def algorithmic(case):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    # The GPU clock ramps up over tens of milliseconds of sustained load: a
+    # few warmup steps would time part of the ramp rather than steady state.
+    ap.add_argument("--warmup", type=int, default=400)
     ap.add_argument("--workload", default="ln_linear_bias_1024x8192")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (e.g. under a profiler)")
