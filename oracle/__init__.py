@@ -25,7 +25,7 @@ _LIB_OVERRIDE = os.environ.get("NORM_GEMM_ORACLE_LIB")
 
 F16, BF16 = 0, 1
 NORM_NONE, NORM_LAYERNORM, NORM_RMSNORM = 0, 1, 2
-ACT_NONE, ACT_SILU = 0, 1
+ACT_NONE, ACT_SILU, ACT_RELU, ACT_GELU = 0, 1, 2, 3
 
 
 def build(force: bool = True) -> str:

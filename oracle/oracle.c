@@ -22,10 +22,18 @@
  *   GEMM       (same page, strategies 1-3): y = a . W^T with W stored [N,K]
  *              and passed as w.T.
  *   bias / act (page 3 above, section 3.3 chain "MatMul -> BiasAdd -> ReLU"):
- *              act(z + bias). SiLU is not defined on the pages; the textbook
- *              z * sigmoid(z) = z / (1 + exp(-z)) is used.
+ *              act(z + bias). The activations are those page 1 names for
+ *              MatMul + activation fusion (section 二 strategy 1, and its
+ *              table of fused GEMM+ReLU / GELU / SiLU instructions); the pages
+ *              define none of them, so the textbook forms are used:
+ *              SiLU z * sigmoid(z) = z / (1 + exp(-z)); ReLU max(z, 0);
+ *              GELU the exact form z * Phi(z) = z / 2 * (1 + erf(z / sqrt 2)),
+ *              Phi the standard normal distribution function.
  *   FFN        (page 1 above, section 二 strategy 2): FFN(x) =
- *              MatMul2(SiLU(MatMul1(x))); the intermediate h is kept in fp64.
+ *              MatMul2(SiLU(MatMul1(x))); page 3's section 3.3 chain
+ *              LayerNorm -> MatMul -> BiasAdd -> ReLU -> MatMul -> BiasAdd is
+ *              the same composition with a norm prologue, biases and another
+ *              activation. The intermediate h is kept in fp64.
  *
  * Every input is the raw 16-bit pattern (IEEE binary16 or bfloat16) that the
  * GPU receives; this file decodes it exactly to double with its own decoder.
@@ -43,7 +51,7 @@
 
 enum { OR_F16 = 0, OR_BF16 = 1 };
 enum { OR_NORM_NONE = 0, OR_NORM_LAYERNORM = 1, OR_NORM_RMSNORM = 2 };
-enum { OR_ACT_NONE = 0, OR_ACT_SILU = 1 };
+enum { OR_ACT_NONE = 0, OR_ACT_SILU = 1, OR_ACT_RELU = 2, OR_ACT_GELU = 3 };
 enum { OR_OK = 0, OR_ERR_ARG = -1, OR_ERR_NOMEM = -2 };
 
 /* IEEE 754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
@@ -139,6 +147,10 @@ static double apply_act(double z, int act)
 {
     if (act == OR_ACT_SILU)
         return z / (1.0 + exp(-z));
+    if (act == OR_ACT_RELU)
+        return z < 0.0 ? 0.0 : z;
+    if (act == OR_ACT_GELU)
+        return 0.5 * z * (1.0 + erf(z / sqrt(2.0)));
     return z;
 }
 
@@ -148,7 +160,7 @@ static int check_common(int64_t M, int64_t K, int norm, int act, int dtype)
         return OR_ERR_ARG;
     if (norm < OR_NORM_NONE || norm > OR_NORM_RMSNORM)
         return OR_ERR_ARG;
-    if (act < OR_ACT_NONE || act > OR_ACT_SILU)
+    if (act < OR_ACT_NONE || act > OR_ACT_GELU)
         return OR_ERR_ARG;
     if (dtype != OR_F16 && dtype != OR_BF16)
         return OR_ERR_ARG;

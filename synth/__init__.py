@@ -29,7 +29,7 @@ import numpy as np
 F16 = 0
 BF16 = 1
 NORM_NONE, NORM_LAYERNORM, NORM_RMSNORM = 0, 1, 2
-ACT_NONE, ACT_SILU = 0, 1
+ACT_NONE, ACT_SILU, ACT_RELU, ACT_GELU = 0, 1, 2, 3
 
 _CHUNK = 1 << 24  # elements per draw; fixed so that results never depend on it
 

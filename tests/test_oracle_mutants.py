@@ -28,6 +28,9 @@ MUTATIONS = {
                        " + (bias ? dec(bias[cols[j]], dtype) : 0.0);"),
     "silu_sign": ("return z / (1.0 + exp(-z));", "return z / (1.0 + exp(z));"),
     "ffn_h_not_activated": ("h[f] = apply_act(z, act);", "h[f] = z;"),
+    "relu_leaky": ("return z < 0.0 ? 0.0 : z;", "return z < 0.0 ? 0.01 * z : z;"),
+    "gelu_erf_unscaled": ("return 0.5 * z * (1.0 + erf(z / sqrt(2.0)));",
+                          "return 0.5 * z * (1.0 + erf(z));"),
     "f16_exponent_bias": ("v = ldexp(1.0 + (double)f / 1024.0, e - 15);",
                           "v = ldexp(1.0 + (double)f / 1024.0, e - 16);"),
     "bf16_fraction": ("v = ldexp(1.0 + (double)f / 128.0, e - 127);",

@@ -137,9 +137,15 @@ def test_gemm_without_norm_matches_numpy_matmul(M, N, K):
     np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12)
 
 
+TORCH_ACT = {oracle.ACT_NONE: lambda z: z, oracle.ACT_SILU: Fn.silu, oracle.ACT_RELU: Fn.relu,
+             oracle.ACT_GELU: lambda z: Fn.gelu(z, approximate="none")}
+
+
 @pytest.mark.parametrize("norm,act", [(oracle.NORM_LAYERNORM, oracle.ACT_NONE),
                                       (oracle.NORM_LAYERNORM, oracle.ACT_SILU),
-                                      (oracle.NORM_RMSNORM, oracle.ACT_SILU)])
+                                      (oracle.NORM_RMSNORM, oracle.ACT_SILU),
+                                      (oracle.NORM_LAYERNORM, oracle.ACT_RELU),
+                                      (oracle.NORM_RMSNORM, oracle.ACT_GELU)])
 @pytest.mark.parametrize("dtype", [synth.F16, synth.BF16])
 def test_full_path_matches_unfused_torch_composition(norm, act, dtype):
     """The pages' op-by-op composition written with library routines in fp64."""
@@ -155,7 +161,7 @@ def test_full_path_matches_unfused_torch_composition(norm, act, dtype):
     A = Fn.layer_norm(X, (K,), G, B, e) if norm == oracle.NORM_LAYERNORM \
         else Fn.rms_norm(X, (K,), G, e) + B
     Z = Fn.linear(A, Wt, Bi)
-    ref = (Fn.silu(Z) if act == oracle.ACT_SILU else Z).numpy()
+    ref = TORCH_ACT[act](Z).numpy()
     np.testing.assert_allclose(y, ref, rtol=1e-11, atol=1e-12)
 
 
@@ -221,6 +227,50 @@ def test_silu_closed_forms_via_zero_weight_and_bias_sweep():
     np.testing.assert_allclose(yneg[0], y[0] - zb, rtol=1e-12, atol=1e-12)
 
 
+# ------------------------------------------------------------ ReLU, GELU
+def _act_sweep(act, zb_values, x_rows=2, K=8, seed=18):
+    """act(bias) through a zero weight: y[m, n] = act(bias[n]) for every row."""
+    bias = f16(zb_values)
+    x = f16(np.random.default_rng(seed).normal(0, 1, (x_rows, K)))
+    W = f16(np.zeros((len(zb_values), K)))
+    y = oracle.norm_gemm(x, None, None, W, bias, 1e-5, oracle.NORM_LAYERNORM, act, synth.F16)
+    return y, val16(bias, synth.F16)
+
+
+def test_relu_closed_form_via_zero_weight_and_bias_sweep():
+    y, zb = _act_sweep(oracle.ACT_RELU, np.linspace(-20, 20, 41))
+    for m in range(y.shape[0]):
+        assert np.array_equal(y[m], np.where(zb < 0, 0.0, zb))
+    # ReLU(z) - ReLU(-z) = z
+    yn, _ = _act_sweep(oracle.ACT_RELU, -zb)
+    np.testing.assert_array_equal(y[0] - yn[0], zb)
+
+
+def test_gelu_closed_forms_via_zero_weight_and_bias_sweep():
+    y, zb = _act_sweep(oracle.ACT_GELU, np.linspace(-8, 8, 33))
+    ref = Fn.gelu(t64(zb), approximate="none").numpy()
+    for m in range(y.shape[0]):
+        np.testing.assert_allclose(y[m], ref, rtol=1e-14, atol=1e-300)
+    # GELU(0) = 0; GELU(z) - GELU(-z) = z (Phi(z) + Phi(-z) = 1)
+    assert y[0][len(zb) // 2] == 0.0
+    yn, _ = _act_sweep(oracle.ACT_GELU, -zb)
+    np.testing.assert_allclose(y[0] - yn[0], zb, rtol=1e-14, atol=1e-14)
+
+
+def test_gelu_at_normal_table_points():
+    with open(os.path.join(GOLDEN, "gelu_normal_table.json"), encoding="utf-8") as f:
+        gd = json.load(f)
+    from scipy.special import ndtr   # an implementation independent of libm's erf
+    for z, p in gd["phi"].items():
+        assert abs(float(ndtr(float(z))) - p) < 1e-15
+        assert abs(1.0 - p - gd["upper_tail"][z]) < 1e-15
+    env = {f"phi{z}": p for z, p in gd["phi"].items()}
+    env.update({f"tail{z}": p for z, p in gd["upper_tail"].items()})
+    ref = np.array([float(eval(s, {"__builtins__": {}}, env)) for s in gd["gelu_expected"]])
+    y, _ = _act_sweep(oracle.ACT_GELU, np.array(gd["gelu_of"]))
+    np.testing.assert_allclose(y[0], ref, rtol=1e-13, atol=0)
+
+
 # ------------------------------------------------------------ hand-worked
 def _golden():
     with open(os.path.join(GOLDEN, "ln_rms_worked_example.json"), encoding="utf-8") as f:
@@ -263,19 +313,26 @@ def test_hand_worked_silu_values():
 
 
 # -------------------------------------------------------------------- FFN
-@pytest.mark.parametrize("norm", [oracle.NORM_NONE, oracle.NORM_LAYERNORM])
-def test_ffn_matches_unfused_torch_composition(norm):
+@pytest.mark.parametrize("norm,act", [(oracle.NORM_NONE, oracle.ACT_SILU),
+                                      (oracle.NORM_LAYERNORM, oracle.ACT_SILU),
+                                      (oracle.NORM_LAYERNORM, oracle.ACT_RELU),
+                                      (oracle.NORM_RMSNORM, oracle.ACT_GELU)])
+def test_ffn_matches_unfused_torch_composition(norm, act):
+    """LayerNorm -> MatMul + bias -> act -> MatMul + bias: with ReLU, the chain
+    of page 3, section 3.3."""
     rng = np.random.default_rng(16)
     M, K, F, N = 5, 19, 23, 11
     x, g, b = f16(rng.normal(0, 1, (M, K))), f16(rng.normal(1, .3, K)), f16(rng.normal(0, .3, K))
     W1, W2 = f16(rng.normal(0, .3, (F, K))), f16(rng.normal(0, .3, (N, F)))
     b1, b2 = f16(rng.normal(0, .3, F)), f16(rng.normal(0, .3, N))
-    y = oracle.ffn(x, g, b, W1, b1, W2, b2, 1e-5, norm, oracle.ACT_SILU, synth.F16)
+    y = oracle.ffn(x, g, b, W1, b1, W2, b2, 1e-5, norm, act, synth.F16)
     X = t64(val16(x, synth.F16))
+    G, B = t64(val16(g, synth.F16)), t64(val16(b, synth.F16))
     if norm == oracle.NORM_LAYERNORM:
-        X = Fn.layer_norm(X, (K,), t64(val16(g, synth.F16)), t64(val16(b, synth.F16)),
-                          float(np.float32(1e-5)))
-    H = Fn.silu(Fn.linear(X, t64(val16(W1, synth.F16)), t64(val16(b1, synth.F16))))
+        X = Fn.layer_norm(X, (K,), G, B, float(np.float32(1e-5)))
+    elif norm == oracle.NORM_RMSNORM:
+        X = Fn.rms_norm(X, (K,), G, float(np.float32(1e-5))) + B
+    H = TORCH_ACT[act](Fn.linear(X, t64(val16(W1, synth.F16)), t64(val16(b1, synth.F16))))
     ref = Fn.linear(H, t64(val16(W2, synth.F16)), t64(val16(b2, synth.F16))).numpy()
     np.testing.assert_allclose(y, ref, rtol=1e-11, atol=1e-12)
 
