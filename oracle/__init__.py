@@ -69,6 +69,8 @@ def lib():
                                  i64, ctypes.c_float, ctypes.c_int, ctypes.c_int,
                                  ctypes.c_int, pi64, i64, pi64, i64, pf64]
         L.oracle_ffn.restype = ctypes.c_int
+        L.oracle_gated_ffn.argtypes = L.oracle_ffn.argtypes
+        L.oracle_gated_ffn.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -144,11 +146,13 @@ def norm_gemm(x, gamma, beta, W, bias, eps: float, norm: int, act: int, dtype: i
 
 def ffn(x, gamma, beta, W1, b1, W2, b2, eps: float, norm: int, act: int, dtype: int,
         rows: Optional[Sequence[int]] = None,
-        cols: Optional[Sequence[int]] = None) -> np.ndarray:
+        cols: Optional[Sequence[int]] = None, gated: bool = False) -> np.ndarray:
+    """y = act(a W1^T + b1) W2^T + b2; gated: W1 = [W_gate; W_up] is [2F, K] and
+    h = act(a W_gate^T + b_gate) * (a W_up^T + b_up)."""
     M, K = x.shape
-    F = W1.shape[0]
+    F = W1.shape[0] // 2 if gated else W1.shape[0]
     N = W2.shape[0]
-    assert W1.shape[1] == K and W2.shape[1] == F
+    assert W1.shape[1] == K and W2.shape[1] == F and (not gated or W1.shape[0] == 2 * F)
     x, px = _u16(x)
     g, pg = _u16(gamma)
     b, pb = _u16(beta)
@@ -159,9 +163,10 @@ def ffn(x, gamma, beta, W1, b1, W2, b2, eps: float, norm: int, act: int, dtype: 
     r, pr = _idx(rows, M)
     c, pc = _idx(cols, N)
     out = np.empty((len(r), len(c)), dtype=np.float64)
-    rc = lib().oracle_ffn(px, pg, pb, pw1, pb1, pw2, pb2, M, K, F, N, eps, norm, act,
-                          dtype, pr, len(r), pc, len(c),
-                          out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
+    fn = lib().oracle_gated_ffn if gated else lib().oracle_ffn
+    rc = fn(px, pg, pb, pw1, pb1, pw2, pb2, M, K, F, N, eps, norm, act,
+            dtype, pr, len(r), pc, len(c),
+            out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
     if rc != 0:
         raise ValueError(f"oracle_ffn failed ({rc})")
     return out
@@ -170,9 +175,9 @@ def ffn(x, gamma, beta, W1, b1, W2, b2, eps: float, norm: int, act: int, dtype: 
 def run_case(case, rows=None, cols=None) -> np.ndarray:
     """Oracle output for a :class:`synth.Case` (optionally a row/col sample)."""
     A = case.arrays
-    if case.kind == "ffn":
+    if case.kind in ("ffn", "gated_ffn"):
         return ffn(A["x"], A.get("gamma"), A.get("beta"), A["W1"], A.get("b1"),
                    A["W2"], A.get("b2"), case.eps, case.norm, case.act, case.dtype,
-                   rows, cols)
+                   rows, cols, gated=case.kind == "gated_ffn")
     return norm_gemm(A["x"], A.get("gamma"), A.get("beta"), A["W"], A.get("bias"),
                      case.eps, case.norm, case.act, case.dtype, rows, cols)

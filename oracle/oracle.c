@@ -231,12 +231,16 @@ int oracle_norm_gemm(const uint16_t *x, const uint16_t *gamma, const uint16_t *b
 /* Fused FFN, unfused definition:
  *   h[f]  = act( sum_k a[k] * W1[f, k] + b1[f] )   for every f < F (fp64, not rounded)
  *   y[n]  = sum_f h[f] * W2[n, f] + b2[n]
- * with a = the (optionally) normalized row of x; y_out is fp64 [n_rows, n_cols]. */
-int oracle_ffn(const uint16_t *x, const uint16_t *gamma, const uint16_t *beta,
-               const uint16_t *W1, const uint16_t *b1, const uint16_t *W2,
-               const uint16_t *b2, int64_t M, int64_t K, int64_t F, int64_t N,
-               float eps, int norm, int act, int dtype, const int64_t *rows,
-               int64_t n_rows, const int64_t *cols, int64_t n_cols, double *y_out)
+ * with a = the (optionally) normalized row of x; y_out is fp64 [n_rows, n_cols].
+ * Gated (gated != 0; page "CANN推理加速库ascend-transformer-boost ATB算子融合实战…",
+ * Llama2 section: the SwiGLU FFN, a SiLU-gated linear unit): W1 is [2F, K],
+ * the gate rows first, then the up rows (b1 likewise [2F]), and
+ *   h[f]  = act( sum_k a[k] W1[f, k] + b1[f] ) * ( sum_k a[k] W1[F + f, k] + b1[F + f] ) */
+static int ffn_impl(const uint16_t *x, const uint16_t *gamma, const uint16_t *beta,
+                    const uint16_t *W1, const uint16_t *b1, const uint16_t *W2,
+                    const uint16_t *b2, int64_t M, int64_t K, int64_t F, int64_t N,
+                    float eps, int norm, int act, int dtype, int gated, const int64_t *rows,
+                    int64_t n_rows, const int64_t *cols, int64_t n_cols, double *y_out)
 {
     if (check_common(M, K, norm, act, dtype) || F < 1 || N < 1 || !x || !W1 ||
         !W2 || !rows || !cols || !y_out)
@@ -268,6 +272,15 @@ int oracle_ffn(const uint16_t *x, const uint16_t *gamma, const uint16_t *beta,
             if (b1)
                 z += dec(b1[f], dtype);
             h[f] = apply_act(z, act);
+            if (gated) {
+                const uint16_t *ur = W1 + (F + f) * K;
+                double u = 0.0;
+                for (int64_t k = 0; k < K; ++k)
+                    u += a[k] * dec(ur[k], dtype);
+                if (b1)
+                    u += dec(b1[F + f], dtype);
+                h[f] *= u;
+            }
         }
 #pragma omp parallel for schedule(dynamic, 16)
         for (int64_t j = 0; j < n_cols; ++j) {
@@ -283,4 +296,24 @@ int oracle_ffn(const uint16_t *x, const uint16_t *gamma, const uint16_t *beta,
     free(a);
     free(h);
     return OR_OK;
+}
+
+int oracle_ffn(const uint16_t *x, const uint16_t *gamma, const uint16_t *beta,
+               const uint16_t *W1, const uint16_t *b1, const uint16_t *W2,
+               const uint16_t *b2, int64_t M, int64_t K, int64_t F, int64_t N,
+               float eps, int norm, int act, int dtype, const int64_t *rows,
+               int64_t n_rows, const int64_t *cols, int64_t n_cols, double *y_out)
+{
+    return ffn_impl(x, gamma, beta, W1, b1, W2, b2, M, K, F, N, eps, norm, act, dtype, 0, rows,
+                    n_rows, cols, n_cols, y_out);
+}
+
+int oracle_gated_ffn(const uint16_t *x, const uint16_t *gamma, const uint16_t *beta,
+                     const uint16_t *W1, const uint16_t *b1, const uint16_t *W2,
+                     const uint16_t *b2, int64_t M, int64_t K, int64_t F, int64_t N,
+                     float eps, int norm, int act, int dtype, const int64_t *rows,
+                     int64_t n_rows, const int64_t *cols, int64_t n_cols, double *y_out)
+{
+    return ffn_impl(x, gamma, beta, W1, b1, W2, b2, M, K, F, N, eps, norm, act, dtype, 1, rows,
+                    n_rows, cols, n_cols, y_out);
 }

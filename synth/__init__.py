@@ -130,6 +130,24 @@ def make_ffn(name: str, M: int, K: int, F: int, N: int, *, dtype: int = F16,
     return Case(name, "ffn", dtype, M, K, N, F, norm, act, eps, arr)
 
 
+def make_gated_ffn(name: str, M: int, K: int, F: int, N: int, *, dtype: int = F16,
+                   norm: int = NORM_NONE, act: int = ACT_SILU, eps: float = 1e-5,
+                   gamma: bool = False, beta: bool = False, b1: bool = False,
+                   b2: bool = False, seed: int = 0) -> Case:
+    """Gated FFN: x[M,K] ~ N(0,1), W1 = [W_gate; W_up] [2F,K] ~ N(0, 1/K),
+    W2[N,F] ~ N(0, 1/F); optional gamma/beta, b1 [2F] and b2 ~ N(0, 0.1)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    arr: Dict[str, Optional[np.ndarray]] = {}
+    arr["x"] = normal_bits(rng, (M, K), 0.0, 1.0, dtype)
+    arr["gamma"] = normal_bits(rng, (K,), 1.0, 0.1, dtype) if gamma else None
+    arr["beta"] = normal_bits(rng, (K,), 0.0, 0.1, dtype) if beta else None
+    arr["W1"] = normal_bits(rng, (2 * F, K), 0.0, 1.0 / K, dtype)
+    arr["W2"] = normal_bits(rng, (N, F), 0.0, 1.0 / F, dtype)
+    arr["b1"] = normal_bits(rng, (2 * F,), 0.0, 0.1, dtype) if b1 else None
+    arr["b2"] = normal_bits(rng, (N,), 0.0, 0.1, dtype) if b2 else None
+    return Case(name, "gated_ffn", dtype, M, K, N, F, norm, act, eps, arr)
+
+
 # The five workloads of the hot path, by what they are.
 def ln_linear_bias_64x256(seed: int = 0) -> Case:
     return make_norm_gemm("ln_linear_bias_x64x256_w256x256_f16", 64, 256, 256,

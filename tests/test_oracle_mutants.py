@@ -28,6 +28,8 @@ MUTATIONS = {
                        " + (bias ? dec(bias[cols[j]], dtype) : 0.0);"),
     "silu_sign": ("return z / (1.0 + exp(-z));", "return z / (1.0 + exp(z));"),
     "ffn_h_not_activated": ("h[f] = apply_act(z, act);", "h[f] = z;"),
+    "gated_up_not_biased": ("u += dec(b1[F + f], dtype);", "u += 0.0 * dec(b1[F + f], dtype);"),
+    "gated_act_of_product": ("h[f] *= u;", "h[f] = apply_act(z * u, act);"),
     "relu_leaky": ("return z < 0.0 ? 0.0 : z;", "return z < 0.0 ? 0.01 * z : z;"),
     "gelu_erf_unscaled": ("return 0.5 * z * (1.0 + erf(z / sqrt(2.0)));",
                           "return 0.5 * z * (1.0 + erf(z));"),

@@ -337,6 +337,48 @@ def test_ffn_matches_unfused_torch_composition(norm, act):
     np.testing.assert_allclose(y, ref, rtol=1e-11, atol=1e-12)
 
 
+@pytest.mark.parametrize("norm,act,bias", [(oracle.NORM_RMSNORM, oracle.ACT_SILU, False),
+                                           (oracle.NORM_LAYERNORM, oracle.ACT_GELU, True),
+                                           (oracle.NORM_NONE, oracle.ACT_SILU, True)])
+def test_gated_ffn_matches_unfused_torch_composition(norm, act, bias):
+    """SwiGLU: down(act(gate(a)) * up(a)) with W1 = [W_gate; W_up]."""
+    rng = np.random.default_rng(19)
+    M, K, F, N = 6, 21, 13, 9
+    x, g, b = f16(rng.normal(0, 1, (M, K))), f16(rng.normal(1, .3, K)), f16(rng.normal(0, .3, K))
+    W1, W2 = f16(rng.normal(0, .3, (2 * F, K))), f16(rng.normal(0, .3, (N, F)))
+    b1 = f16(rng.normal(0, .3, 2 * F)) if bias else None
+    b2 = f16(rng.normal(0, .3, N)) if bias else None
+    y = oracle.ffn(x, g, b, W1, b1, W2, b2, 1e-5, norm, act, synth.F16, gated=True)
+    X = t64(val16(x, synth.F16))
+    G, B = t64(val16(g, synth.F16)), t64(val16(b, synth.F16))
+    if norm == oracle.NORM_LAYERNORM:
+        X = Fn.layer_norm(X, (K,), G, B, float(np.float32(1e-5)))
+    elif norm == oracle.NORM_RMSNORM:
+        X = Fn.rms_norm(X, (K,), G, float(np.float32(1e-5))) + B
+    Wt = t64(val16(W1, synth.F16))
+    Bt = t64(val16(b1, synth.F16)) if bias else torch.zeros(2 * F, dtype=torch.float64)
+    gate, up = Fn.linear(X, Wt[:F], Bt[:F]), Fn.linear(X, Wt[F:], Bt[F:])
+    B2 = t64(val16(b2, synth.F16)) if bias else None
+    ref = Fn.linear(TORCH_ACT[act](gate) * up, t64(val16(W2, synth.F16)), B2).numpy()
+    np.testing.assert_allclose(y, ref, rtol=1e-11, atol=1e-12)
+
+
+def test_gated_ffn_with_unit_up_projection_is_the_plain_ffn():
+    """W_up = 0 and b_up = 1 make the gate factor 1: the ungated FFN."""
+    rng = np.random.default_rng(20)
+    M, K, F, N = 5, 16, 11, 7
+    x = f16(rng.normal(0, 1, (M, K)))
+    Wg, W2 = f16(rng.normal(0, .3, (F, K))), f16(rng.normal(0, .3, (N, F)))
+    bg = f16(rng.normal(0, .3, F))
+    W1 = np.concatenate([Wg, f16(np.zeros((F, K)))])
+    b1 = np.concatenate([bg, f16(np.ones(F))])
+    y = oracle.ffn(x, None, None, W1, b1, W2, None, 1e-5, oracle.NORM_NONE, oracle.ACT_SILU,
+                   synth.F16, gated=True)
+    ref = oracle.ffn(x, None, None, Wg, bg, W2, None, 1e-5, oracle.NORM_NONE, oracle.ACT_SILU,
+                     synth.F16)
+    np.testing.assert_array_equal(y, ref)
+
+
 def test_ffn_equals_two_norm_gemm_calls_with_unrounded_h():
     rng = np.random.default_rng(17)
     M, K, F, N = 4, 16, 12, 9
