@@ -209,7 +209,7 @@ def main():
         "config": {"workload": case.name, "M": case.M, "K": case.K, "N": case.N,
                    **({"F": case.F} if is_ffn else {}),
                    "norm": ["none", "layernorm", "rmsnorm"][case.norm],
-                   "act": ["none", "silu"][case.act],
+                   "act": ["none", "silu", "relu", "gelu"][case.act],
                    "bias": (A.get("bias") is not None) or (A.get("b1") is not None),
                    "eps": case.eps, "launches_per_step": 2 if is_ffn else 1},
         "roofline": roof,

@@ -16,7 +16,12 @@
  * normalized activation exists only in on-chip memory and registers: it is
  * never written to device memory. Products accumulate in fp32; the epilogue
  * adds bias, applies the activation in fp32 and rounds once to the output
- * type. act = SiLU is z / (1 + exp(-z)).
+ * type. The activations are those page "昇腾CANN的MatMul融合玩法…" names for
+ * MatMul + activation fusion (section 二 strategy 1: ReLU, GELU, SiLU); the
+ * pages define none of them, so the textbook forms are used:
+ *     SiLU  z / (1 + exp(-z))
+ *     ReLU  max(z, 0)
+ *     GELU  z * Phi(z) = z / 2 * (1 + erf(z / sqrt 2))   (exact, not tanh)
  *
  * Conventions for every entry point:
  *  - All tensor pointers are caller-owned DEVICE memory on the current HIP
@@ -48,10 +53,10 @@
 extern "C" {
 #endif
 
-#define NORM_GEMM_ABI_VERSION 1
+#define NORM_GEMM_ABI_VERSION 2   /* 2: NG_ACT_RELU, NG_ACT_GELU */
 
 typedef enum { NG_NORM_NONE = 0, NG_NORM_LAYERNORM = 1, NG_NORM_RMSNORM = 2 } ng_norm_t;
-typedef enum { NG_ACT_NONE = 0, NG_ACT_SILU = 1 } ng_act_t;
+typedef enum { NG_ACT_NONE = 0, NG_ACT_SILU = 1, NG_ACT_RELU = 2, NG_ACT_GELU = 3 } ng_act_t;
 typedef enum { NG_DTYPE_F16 = 0, NG_DTYPE_BF16 = 1 } ng_dtype_t;
 
 typedef enum {
@@ -69,8 +74,9 @@ typedef enum {
 
 /*
  * fused_norm_gemm: y[M,N] = act( norm_affine(x)[M,K] . W[N,K]^T + bias[N] ).
- * One kernel launch. M <= 32 runs the skinny (decode) kernel that streams W
- * once; larger M runs the tiled MFMA kernel. Returns an ng_status_t.
+ * M <= 32 runs the skinny (decode) kernel that streams W once, one launch;
+ * larger M runs the tiled MFMA kernel, preceded for LayerNorm / RMSNorm by a
+ * row-statistics launch on the same stream. Returns an ng_status_t.
  */
 int fused_norm_gemm(const void *x, const void *gamma, const void *beta,
                     const void *W, const void *bias, void *y,
@@ -80,7 +86,10 @@ int fused_norm_gemm(const void *x, const void *gamma, const void *beta,
 /*
  * Fused FFN (page "昇腾CANN的MatMul融合玩法，让大模型推理快3倍", section 二,
  * strategy 2: FFN(x) = MatMul2(SiLU(MatMul1(x)))), with an optional
- * normalization prologue and optional biases:
+ * normalization prologue, optional biases and any activation: with LayerNorm,
+ * biases and ReLU it is the chain LayerNorm -> MatMul -> BiasAdd -> ReLU ->
+ * MatMul -> BiasAdd of page "LayerNorm 融合算子如何让大模型推理再快 15%？深度拆解
+ * ATB 的实现", section 3.3:
  *
  *     h[M,F] = act( norm_affine(x)[M,K] . W1[F,K]^T + b1[F] )   (stored as dtype)
  *     y[M,N] = h . W2[N,F]^T + b2[N]

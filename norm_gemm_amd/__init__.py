@@ -26,7 +26,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY_PATH = os.path.join(_HERE, "libnormgemm.so")
 
 NORMS = {"none": 0, "layernorm": 1, "rmsnorm": 2}
-ACTS = {"none": 0, "silu": 1}
+ACTS = {"none": 0, "silu": 1, "relu": 2, "gelu": 3}
 DTYPES = {torch.float16: 0, torch.bfloat16: 1}
 
 # Symbols declared in include/norm_gemm.h.

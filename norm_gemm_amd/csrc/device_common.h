@@ -128,13 +128,19 @@ __device__ __forceinline__ float wave_sum(float v)
 }
 
 // ----------------------------------------------------------- epilogue
-enum { ACT_NONE = 0, ACT_SILU = 1 };
+enum { ACT_NONE = 0, ACT_SILU = 1, ACT_RELU = 2, ACT_GELU = 3 };
 
-// SiLU(z) = z * sigmoid(z) = z / (1 + e^-z); exp from the device library.
+// SiLU(z) = z * sigmoid(z) = z / (1 + e^-z); ReLU(z) = max(z, 0) (NaN stays
+// NaN); GELU(z) = z * Phi(z) = z / 2 * (1 + erf(z / sqrt 2)), the exact form.
+// exp and erf from the device library.
 __device__ __forceinline__ float apply_act(float z, int act)
 {
     if (act == ACT_SILU)
         return z / (1.0f + __expf(-z));
+    if (act == ACT_RELU)
+        return z < 0.0f ? 0.0f : z;
+    if (act == ACT_GELU)
+        return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
     return z;
 }
 

@@ -35,7 +35,7 @@ static int mul_ok(int64_t a, int64_t b)
 static int enums_ok(int norm, int act, int dtype)
 {
     return norm >= NG_NORM_NONE && norm <= NG_NORM_RMSNORM && act >= NG_ACT_NONE &&
-           act <= NG_ACT_SILU && (dtype == NG_DTYPE_F16 || dtype == NG_DTYPE_BF16);
+           act <= NG_ACT_GELU && (dtype == NG_DTYPE_F16 || dtype == NG_DTYPE_BF16);
 }
 
 static int dim_ok(int64_t d)

@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert ng.norm_gemm_abi_version() == 1
+    assert ng.norm_gemm_abi_version() == 2
     for s in (OK, NULL, SHAPE, ENUM, EPS, ALIAS, WORKSPACE, UNSUP, ALIGN, HIP):
         assert ng.norm_gemm_status_string(s)
     assert ng.norm_gemm_status_string(12345) == "unknown status"
@@ -67,7 +67,7 @@ def gemm(x=X, g=G, b=B, w=W, bias=BI, y=Y, M=4, N=8, K=16, eps=1e-5, norm=1, act
 
 @pytest.mark.parametrize("kw,status", [
     (dict(x=None), NULL), (dict(w=None), NULL), (dict(y=None), NULL),
-    (dict(norm=3), ENUM), (dict(norm=-1), ENUM), (dict(act=2), ENUM), (dict(dtype=2), ENUM),
+    (dict(norm=3), ENUM), (dict(norm=-1), ENUM), (dict(act=4), ENUM), (dict(dtype=2), ENUM),
     (dict(M=0), SHAPE), (dict(N=0), SHAPE), (dict(K=0), SHAPE), (dict(M=-5), SHAPE),
     (dict(K=2 ** 31), SHAPE), (dict(M=2 ** 31 - 1, N=2 ** 31 - 1, K=2 ** 31 - 1), SHAPE),
     (dict(eps=float("nan")), EPS), (dict(eps=float("inf")), EPS), (dict(eps=-1e-6), EPS),

@@ -231,6 +231,46 @@ def test_silu_closed_form_and_zero(M):
     assert np.all(z == 0.0) and not np.any(np.signbit(z))
 
 
+# ------------------------------------------------------ ReLU / GELU epilogues
+RELU, GELU = synth.ACT_RELU, synth.ACT_GELU
+
+# One shape per kernel: LDS prefill (aligned, M > 32; fp16 and bf16), generic
+# prefill (K % 8 != 0), 512-byte-piece decode (M <= 16), line decode
+# (M <= 32), element-load decode (K % 8 != 0).
+ACT_SHAPES = [(129, 300, 264, LN, F16), (257, 513, 520, RMS, BF16), (65, 129, 257, LN, BF16),
+              (8, 1000, 2048, RMS, BF16), (32, 1000, 2048, LN, F16), (3, 100, 37, NONE, F16)]
+
+
+@pytest.mark.parametrize("act", [RELU, GELU])
+@pytest.mark.parametrize("M,N,K,norm,dtype", ACT_SHAPES)
+def test_relu_gelu_epilogues(M, N, K, norm, dtype, act):
+    case = synth.make_norm_gemm(f"act{act}_{M}x{N}x{K}_n{norm}d{dtype}", M, K, N, dtype=dtype,
+                                norm=norm, act=act, eps=1e-5, seed=M + 3 * N + K + act)
+    check_full(case)
+
+
+@pytest.mark.parametrize("M", [4, 64])
+@pytest.mark.parametrize("act", ["relu", "gelu"])
+def test_relu_gelu_closed_forms_and_zero(M, act):
+    """act(bias) through a zero weight, against the oracle at one fp16 rounding
+    (1e-3, ten times tighter than the acceptance bar); act(0) = +0."""
+    import norm_gemm_amd as ng
+    K, N = 64, 81
+    bias = synth.f32_to_f16_bits(np.linspace(-8, 8, N, dtype=np.float32))
+    x = synth.normal_bits(np.random.default_rng(9), (M, K), 0.0, 1.0, F16)
+    W0 = np.zeros((N, K), np.uint16)
+    y = ng.fused_norm_gemm(upload(x, F16), upload(W0, F16), bias=upload(bias, F16), norm=LN,
+                           act=act)
+    y0 = ng.fused_norm_gemm(upload(x, F16), upload(W0, F16), norm=LN, act=act)
+    torch.cuda.synchronize()
+    ref = oracle.norm_gemm(x, None, None, W0, bias, 1e-5, LN, ng.ACTS[act], F16)
+    assert_close(to_f64(y), ref, tol=1e-3, what=f"{act}(bias)")
+    if act == "relu":
+        assert np.array_equal(to_f64(y), ref)     # exact: max(z, 0) of an fp16 value
+    z = to_f64(y0)
+    assert np.all(z == 0.0) and not np.any(np.signbit(z))
+
+
 # ------------------------------------------- persistent tiles / statistics reuse
 @pytest.mark.parametrize("M,N,K,norm", [
     (256, 34816, 64, LN),     # 2 x 136 tiles: XCD-grouped, two rounds, stats reused
@@ -293,6 +333,19 @@ def test_ffn_small(M, K, F, N, norm):
     check_full(case)
 
 
+@pytest.mark.parametrize("M,K,F,N,norm,act", [(33, 72, 130, 33, LN, RELU),
+                                              (100, 264, 520, 136, LN, RELU),
+                                              (20, 136, 200, 72, RMS, GELU),
+                                              (70, 256, 384, 128, NONE, GELU)])
+def test_ffn_chain_norm_bias_act(M, K, F, N, norm, act):
+    """LayerNorm -> MatMul + bias -> ReLU -> MatMul + bias (the chain of page
+    3, section 3.3) and its RMSNorm / GELU variants through fused_ffn."""
+    case = synth.make_ffn(f"ffn_chain_{M}x{K}x{F}x{N}_n{norm}a{act}", M, K, F, N, norm=norm,
+                          act=act, gamma=norm != NONE, beta=norm == LN, b1=True, b2=True,
+                          seed=M + K + F + N)
+    check_full(case)
+
+
 @pytest.mark.parametrize("M", [16, 100])
 def test_ffn_equals_two_norm_gemm_calls(M):
     import norm_gemm_amd as ng
@@ -332,6 +385,15 @@ def test_full_rms_matmul_silu_512x14336():
 
 def test_full_ffn_silu_512x14336x49152():
     check_sampled(synth.ffn_silu_512x14336x49152(), 2, 200)
+
+
+def test_ffn_chain_ln_relu_bias_1024x8192():
+    """The page-3 chain at its example's width: x[8 x 128, 8192], LayerNorm,
+    MatMul 8192 -> 8192 + bias, ReLU, MatMul 8192 -> 8192 + bias."""
+    case = synth.make_ffn("ffn_chain_ln_relu_x1024x8192_w1_8192_w2_8192_f16", 1024, 8192, 8192,
+                          8192, norm=LN, act=RELU, gamma=True, beta=True, b1=True, b2=True,
+                          seed=0)
+    check_sampled(case, 4, 300)
 
 
 @pytest.mark.parametrize("M", [1, 8, 32])
