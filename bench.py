@@ -87,6 +87,9 @@ def algorithmic(case):
     if case.kind == "ffn":
         F = case.F
         return 2 * M * K * F + 2 * M * F * N, nbytes + M * N * 2
+    if case.kind == "gated_ffn":
+        F = case.F
+        return 2 * M * K * 2 * F + 2 * M * F * N, nbytes + M * N * 2
     return 2 * M * N * K, nbytes + M * N * 2
 
 
@@ -117,7 +120,10 @@ def main():
     torch.cuda.set_device(dev)
     A = case.arrays
     flops, nbytes = algorithmic(case)
-    is_ffn = case.kind == "ffn"
+    is_ffn = case.kind in ("ffn", "gated_ffn")
+    ffn_call = ng.fused_gated_ffn if case.kind == "gated_ffn" else ng.fused_ffn
+    ws_size = (ng.fused_gated_ffn_workspace_size if case.kind == "gated_ffn"
+               else ng.fused_ffn_workspace_size)
     wkeys = ("W1", "W2") if is_ffn else ("W",)
     wbytes = sum(A[k].size * 2 for k in wkeys)
     copies = max(2, math.ceil(1.5 * LLC_BYTES / wbytes) + 1)
@@ -130,15 +136,15 @@ def main():
     out = torch.empty(case.M, case.N, dtype=up["x"].dtype, device=dev)
     ws = None
     if is_ffn:
-        ws = torch.empty(ng.fused_ffn_workspace_size(case.M, case.F, up["x"].dtype),
+        ws = torch.empty(ws_size(case.M, case.F, up["x"].dtype),
                          dtype=torch.uint8, device=dev)
 
     def step(i):
         w = wsets[i % copies]
         if is_ffn:
-            ng.fused_ffn(get("x"), w["W1"], w["W2"], get("gamma"), get("beta"), get("b1"),
-                         get("b2"), eps=case.eps, norm=case.norm, act=case.act,
-                         workspace=ws, out=out)
+            ffn_call(get("x"), w["W1"], w["W2"], get("gamma"), get("beta"), get("b1"),
+                     get("b2"), eps=case.eps, norm=case.norm, act=case.act,
+                     workspace=ws, out=out)
         else:
             ng.fused_norm_gemm(get("x"), w["W"], get("gamma"), get("beta"), get("bias"),
                                eps=case.eps, norm=case.norm, act=case.act, out=out)
@@ -209,9 +215,10 @@ def main():
         "config": {"workload": case.name, "M": case.M, "K": case.K, "N": case.N,
                    **({"F": case.F} if is_ffn else {}),
                    "norm": ["none", "layernorm", "rmsnorm"][case.norm],
-                   "act": ["none", "silu", "relu", "gelu"][case.act],
+                   "act": ["none", "silu", "relu", "gelu"][case.act], "gated": case.kind == "gated_ffn",
                    "bias": (A.get("bias") is not None) or (A.get("b1") is not None),
-                   "eps": case.eps, "launches_per_step": 2 if is_ffn else 1},
+                   "eps": case.eps,
+                   "launches_per_step": (2 if is_ffn else 1) + (1 if case.norm and case.M > 32 else 0)},
         "roofline": roof,
         "cpu_baseline": cpu,
         "timing": {"avg_launch_ms": round(avg_launch_ms, 5),

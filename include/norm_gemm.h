@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define NORM_GEMM_ABI_VERSION 2   /* 2: NG_ACT_RELU, NG_ACT_GELU */
+#define NORM_GEMM_ABI_VERSION 3   /* 2: NG_ACT_RELU, NG_ACT_GELU; 3: fused_gated_ffn */
 
 typedef enum { NG_NORM_NONE = 0, NG_NORM_LAYERNORM = 1, NG_NORM_RMSNORM = 2 } ng_norm_t;
 typedef enum { NG_ACT_NONE = 0, NG_ACT_SILU = 1, NG_ACT_RELU = 2, NG_ACT_GELU = 3 } ng_act_t;
@@ -107,6 +107,33 @@ int fused_ffn(const void *x, const void *gamma, const void *beta,
               void *y, int64_t M, int64_t K, int64_t F, int64_t N,
               float eps, int norm, int act, int dtype,
               void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Gated FFN (page "CANN推理加速库ascend-transformer-boost ATB算子融合实战…", Llama2
+ * section: the FFN's SwiGLU, a SiLU-gated linear unit, fused with its
+ * MatMuls), with the same optional normalization prologue and biases:
+ *
+ *     a       = norm_affine(x)[M,K]
+ *     h[M,F]  = act( a . W_gate^T + b_gate ) * ( a . W_up^T + b_up )   (stored as dtype)
+ *     y[M,N]  = h . W2[N,F]^T + b2[N]
+ *
+ * W1 is [2F, K]: the F gate rows first, then the F up rows (one concatenated
+ * projection); b1, when given, is [2F] in the same order. act = SiLU gives
+ * SwiGLU. For M > 32 with 16-byte aligned operands and K % 8 == 0, phase 1
+ * is one tiled kernel whose tiles hold the gate and up rows of the same
+ * output columns, so g and u meet in registers and only h is written. Else
+ * the [gate | up] projections of every row go to the workspace and a second
+ * kernel forms h. The workspace must hold fused_gated_ffn_workspace_size(M,
+ * F, dtype) bytes (3 M F elements: h, then the [M, 2F] projections); other
+ * conventions as fused_ffn. Returns an ng_status_t.
+ */
+size_t fused_gated_ffn_workspace_size(int64_t M, int64_t F, int dtype);
+
+int fused_gated_ffn(const void *x, const void *gamma, const void *beta,
+                    const void *W1, const void *b1, const void *W2, const void *b2,
+                    void *y, int64_t M, int64_t K, int64_t F, int64_t N,
+                    float eps, int norm, int act, int dtype,
+                    void *workspace, size_t workspace_bytes, void *stream);
 
 /* Human-readable text of a status code (static storage, never NULL). */
 const char *norm_gemm_status_string(int status);

@@ -30,8 +30,8 @@ ACTS = {"none": 0, "silu": 1, "relu": 2, "gelu": 3}
 DTYPES = {torch.float16: 0, torch.bfloat16: 1}
 
 # Symbols declared in include/norm_gemm.h.
-EXPORTED = ("fused_norm_gemm", "fused_ffn", "fused_ffn_workspace_size",
-            "norm_gemm_status_string", "norm_gemm_abi_version")
+EXPORTED = ("fused_norm_gemm", "fused_ffn", "fused_ffn_workspace_size", "fused_gated_ffn",
+            "fused_gated_ffn_workspace_size", "norm_gemm_status_string", "norm_gemm_abi_version")
 
 
 class NormGemmError(RuntimeError):
@@ -52,6 +52,10 @@ def _load() -> ctypes.CDLL:
     L.fused_ffn.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, f32, ci, ci,
                             ci, vp, sz, vp]
     L.fused_ffn.restype = ci
+    L.fused_gated_ffn_workspace_size.argtypes = [i64, i64, ci]
+    L.fused_gated_ffn_workspace_size.restype = sz
+    L.fused_gated_ffn.argtypes = L.fused_ffn.argtypes
+    L.fused_gated_ffn.restype = ci
     L.norm_gemm_status_string.argtypes = [ci]
     L.norm_gemm_status_string.restype = ctypes.c_char_p
     L.norm_gemm_abi_version.argtypes = []
@@ -73,6 +77,11 @@ def norm_gemm_abi_version() -> int:
 def fused_ffn_workspace_size(M: int, F: int, dtype) -> int:
     d = DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
     return int(lib.fused_ffn_workspace_size(int(M), int(F), d))
+
+
+def fused_gated_ffn_workspace_size(M: int, F: int, dtype) -> int:
+    d = DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(lib.fused_gated_ffn_workspace_size(int(M), int(F), d))
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -156,6 +165,26 @@ def fused_ffn(x: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor,
     The intermediate h[M, F] lives in ``workspace`` (a uint8 device tensor of
     at least :func:`fused_ffn_workspace_size` bytes; allocated when not given).
     """
+    return _ffn(False, x, w1, w2, gamma, beta, b1, b2, eps, norm, act, workspace, out, stream)
+
+
+def fused_gated_ffn(x: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor,
+                    gamma: Optional[torch.Tensor] = None, beta: Optional[torch.Tensor] = None,
+                    b1: Optional[torch.Tensor] = None, b2: Optional[torch.Tensor] = None, *,
+                    eps: float = 1e-5, norm="none", act="silu",
+                    workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                    stream=None) -> torch.Tensor:
+    """Gated FFN (SwiGLU with act="silu"): with w1 = [w_gate; w_up] of shape
+    [2F, K] (and b1 = [b_gate; b_up] of shape [2F]),
+    y = (act(a @ w_gate.T + b_gate) * (a @ w_up.T + b_up)) @ w2[N, F].T + b2,
+    a = norm_affine(x). The workspace holds at least
+    :func:`fused_gated_ffn_workspace_size` bytes (allocated when not given).
+    """
+    return _ffn(True, x, w1, w2, gamma, beta, b1, b2, eps, norm, act, workspace, out, stream)
+
+
+def _ffn(gated, x, w1, w2, gamma, beta, b1, b2, eps, norm, act, workspace, out, stream):
+    what = "fused_gated_ffn" if gated else "fused_ffn"
     if not isinstance(x, torch.Tensor) or x.dim() < 1:
         raise ValueError("x must be a tensor with at least one dimension")
     if x.dtype not in DTYPES:
@@ -163,16 +192,16 @@ def fused_ffn(x: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor,
     dev = x.device
     K = x.shape[-1]
     M = x.numel() // K if K else 0
-    if w1 is None or w1.dim() != 2 or w1.shape[1] != K:
-        raise ValueError(f"w1 must be [F, {K}]")
-    F = w1.shape[0]
+    if w1 is None or w1.dim() != 2 or w1.shape[1] != K or (gated and w1.shape[0] % 2):
+        raise ValueError(f"w1 must be [{'2F' if gated else 'F'}, {K}]")
+    F = w1.shape[0] // 2 if gated else w1.shape[0]
     if w2 is None or w2.dim() != 2 or w2.shape[1] != F:
         raise ValueError(f"w2 must be [N, {F}]")
     N = w2.shape[0]
     for t, name, shp in ((x, "x", None), (w1, "w1", None), (w2, "w2", None), (gamma, "gamma", (K,)),
-                         (beta, "beta", (K,)), (b1, "b1", (F,)), (b2, "b2", (N,))):
+                         (beta, "beta", (K,)), (b1, "b1", (w1.shape[0],)), (b2, "b2", (N,))):
         _check(t, name, x.dtype, dev, shp)
-    need = fused_ffn_workspace_size(M, F, x.dtype)
+    need = (fused_gated_ffn_workspace_size if gated else fused_ffn_workspace_size)(M, F, x.dtype)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     if workspace.device != dev or not workspace.is_contiguous():
@@ -183,10 +212,11 @@ def fused_ffn(x: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor,
     _check(out, "out", x.dtype, dev, lead + (N,))
     ws_bytes = workspace.numel() * workspace.element_size()
     with torch.cuda.device(dev):
-        st = lib.fused_ffn(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(w1), _ptr(b1), _ptr(w2),
-                           _ptr(b2), _ptr(out), M, K, F, N, float(eps),
-                           _enum(NORMS, norm, "norm"), _enum(ACTS, act, "act"),
-                           DTYPES[x.dtype], _ptr(workspace), ws_bytes, _stream(dev, stream))
+        fn = lib.fused_gated_ffn if gated else lib.fused_ffn
+        st = fn(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(w1), _ptr(b1), _ptr(w2),
+                _ptr(b2), _ptr(out), M, K, F, N, float(eps),
+                _enum(NORMS, norm, "norm"), _enum(ACTS, act, "act"),
+                DTYPES[x.dtype], _ptr(workspace), ws_bytes, _stream(dev, stream))
     if st != 0:
-        raise NormGemmError(st, "fused_ffn")
+        raise NormGemmError(st, what)
     return out

@@ -84,6 +84,44 @@ int fused_ffn(const void *x, const void *gamma, const void *beta, const void *W1
                s);
 }
 
+size_t fused_gated_ffn_workspace_size(int64_t M, int64_t F, int dtype)
+{
+    return ng_gated_ffn_workspace_size(M, F, dtype);
+}
+
+int fused_gated_ffn(const void *x, const void *gamma, const void *beta, const void *W1,
+                    const void *b1, const void *W2, const void *b2, void *y, int64_t M,
+                    int64_t K, int64_t F, int64_t N, float eps, int norm, int act, int dtype,
+                    void *workspace, size_t workspace_bytes, void *stream)
+{
+    int st = ng_validate_gated_ffn(x, gamma, beta, W1, b1, W2, b2, y, M, K, F, N, eps, norm,
+                                   act, dtype, workspace, workspace_bytes);
+    if (st != NG_OK)
+        return st;
+    hipStream_t s = (hipStream_t)stream;
+    char *h = (char *)workspace;
+    // phase 1: h = act(a . W_gate^T + b_gate) * (a . W_up^T + b_up)
+    const ng::GemmArgs a = make_args(x, gamma, beta, W1, b1, h, M, F, K, eps, norm, act, dtype);
+    if (ng::prefill_gated_fits(a)) {
+        if (ng::launch_prefill_lds_gated(a, s) != hipSuccess)
+            return NG_ERR_HIP;
+    } else {
+        // the [gate | up] projections of every row, then the gating
+        void *gu = h + (size_t)M * (size_t)F * 2u;
+        st = run(make_args(x, gamma, beta, W1, b1, gu, M, 2 * F, K, eps, norm, NG_ACT_NONE,
+                           dtype),
+                 s);
+        if (st != NG_OK)
+            return st;
+        if (ng::launch_gate(gu, h, M, F, act, dtype, s) != hipSuccess)
+            return NG_ERR_HIP;
+    }
+    // phase 2: y = h . W2^T + b2
+    return run(make_args(h, nullptr, nullptr, W2, b2, y, M, N, F, 0.0f, NG_NORM_NONE,
+                         NG_ACT_NONE, dtype),
+               s);
+}
+
 const char *norm_gemm_status_string(int status)
 {
     switch (status) {

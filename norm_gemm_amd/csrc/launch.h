@@ -22,6 +22,12 @@ hipError_t launch_decode(const GemmArgs &a, hipStream_t s);      // any alignmen
 hipError_t launch_decode_lds(const GemmArgs &a, hipStream_t s);  // a.vec only
 hipError_t launch_decode_wide(const GemmArgs &a, hipStream_t s); // a.vec and decode_wide_fits
 bool decode_wide_fits(const GemmArgs &a);  // M <= 16, N >= 16, 32-bit slab offsets
+// gated tiled kernel: a.W = [W_gate; W_up] is [2 a.N, a.K], a.bias [2 a.N]
+bool prefill_gated_fits(const GemmArgs &a);  // a.vec, M > 32, 32-bit W row offsets
+hipError_t launch_prefill_lds_gated(const GemmArgs &a, hipStream_t s);
+// h[M, F] = act(gu[:, :F]) * gu[:, F:] for gu[M, 2F]
+hipError_t launch_gate(const void *gu, void *h, int64_t M, int64_t F, int act, int dtype,
+                       hipStream_t s);
 
 constexpr int64_t kDecodeMaxM = 32;
 

@@ -118,7 +118,7 @@ enum { ST_NONE = 0, ST_PROLOGUE = 1, ST_FROM_Y = 2 };
 // Row-statistics pass for ST_FROM_Y: one wave per row of x, one pass over the
 // row with 128-bit loads and packed dot products accumulating in fp32, a wave
 // reduction, then (rs, nmr) as two floats written into the first 8 bytes of
-// the row's slice of every 256-column output tile of y. Each tile of the main
+// the row's slice of every tw-column output tile of y. Each tile of the main
 // kernel reads these 8 bytes of its own rows before it writes its own tile,
 // so y serves as per-tile scratch and no workgroup reads memory that another
 // one writes. Only the statistics pass through device memory; the normalized
@@ -127,7 +127,7 @@ template <int DT>
 __global__ __launch_bounds__(256) void row_stats_to_y_kernel(const uint16_t *__restrict__ x,
                                                              uint16_t *__restrict__ y, int M,
                                                              int N, int K, float eps, int norm,
-                                                             int tn)
+                                                             int tn, int tw)
 {
     const int lane = threadIdx.x & 63;
     const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -167,13 +167,14 @@ __global__ __launch_bounds__(256) void row_stats_to_y_kernel(const uint16_t *__r
     finish_stats(s1, s2, bits_to_f<DT>((uint16_t)s0), K, eps, ln, rs, nmr);
     const uint2 pk = make_uint2(__builtin_bit_cast(uint32_t, rs), __builtin_bit_cast(uint32_t, nmr));
     for (int t = lane; t < tn; t += 64)
-        *reinterpret_cast<uint2 *>(y + (int64_t)m * N + (int64_t)t * BN) = pk;
+        *reinterpret_cast<uint2 *>(y + (int64_t)m * N + (int64_t)t * tw) = pk;
 }
 
 // GB: bit 0 gamma present, bit 1 beta present (with STATS != ST_NONE);
 // KT: K % 64 != 0 (the last K step is ragged); LN: LayerNorm (else RMSNorm,
-// with STATS != ST_NONE).
-template <int DT, int STATS, int GB, bool KT, bool LN>
+// with STATS != ST_NONE); GT: gated output (see the gated epilogue): W is
+// [2N, K] = [W_gate; W_up], bias [2N], and a tile covers 128 output columns.
+template <int DT, int STATS, int GB, bool KT, bool LN, bool GT>
 __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ gamma,
     const uint16_t *__restrict__ beta, const uint16_t *__restrict__ W,
@@ -218,9 +219,12 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
     const int nk = (K + BK - 1) / BK;
     constexpr bool k_tail = KT;
 
+    // output columns per tile: 256, or 128 gated (the 256 W rows of a tile are
+    // the gate and up rows of the same 128 columns)
+    constexpr int BNO = GT ? BN / 2 : BN;
     int mb, nt;
     tile_of(mp, blockIdx.x, mb, nt);
-    const int m0 = mb * BM, n0 = nt * BN;
+    const int m0 = mb * BM, n0 = nt * BNO;
 
     // ---- direct HBM -> LDS loads. Instruction i of a wave fills 8 tile rows
     // (x: i*A_IST + wave*8 .., W: wave*B_RPW + i*8 ..); lane l lands at chunk
@@ -246,7 +250,18 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
     for (int i = 0; i < B_DMA; ++i) {
         const int row = wave * B_RPW + i * 8 + (lane >> 3);
         wch[i] = swz(row, lane & 7);
-        const uint32_t rb = (uint32_t)(min(n0 + row, N - 1) - n0) * (uint32_t)K;
+        // W row of tile row `row`, relative to n0. Gated: tile rows 64 w + r
+        // (r < 32) hold the gate row of output column 32 w + r and rows
+        // 64 w + 32 + r the up row of the same column, so that each wave's
+        // two 32-row MFMA blocks are the gate and up halves of its columns.
+        int src;
+        if constexpr (GT) {
+            const int f = min(n0 + (row >> 6) * 32 + (row & 31), N - 1) - n0;
+            src = (row & 32) ? N + f : f;
+        } else {
+            src = min(n0 + row, N - 1) - n0;
+        }
+        const uint32_t rb = (uint32_t)src * (uint32_t)K;
         woff[i] = (rb + wch[i] * 8) * 2u;
         woff_t[i] = (rb + tail_chunk(wch[i]) * 8) * 2u;
     }
@@ -660,6 +675,56 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
     wait_vmcnt<0>();
     __syncthreads();
 
+    if constexpr (GT) {
+        // ---- gated epilogue: each lane holds the gate (j = 0) and up (j = 1)
+        // sums of the same output elements; h = act(gate + b_gate) *
+        // (up + b_up) in fp32, one rounding, staged row-major in B0 (128 rows
+        // x 16 chunks, 16-byte chunks XOR-swizzled by row), then written with
+        // 128-bit stores
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int nl = wn * 32 + q * 8 + lk * 4;          // column within the tile
+            float bg[4], bu[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int n = n0 + nl + r;
+                const bool ok = bias && n < N;
+                bg[r] = ok ? bits_to_f<DT>(bias[n]) : 0.0f;
+                bu[r] = ok ? bits_to_f<DT>(bias[N + n]) : 0.0f;
+            }
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int ml = wm * WM + i * 32 + lrow;       // row within the tile
+                float v[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    v[r] = apply_act(acc[0][i][q * 4 + r] + bg[r], act) *
+                           (acc[1][i][q * 4 + r] + bu[r]);
+                const int chunk = (nl >> 3) ^ (ml & 15);
+                uint32_t *dst = reinterpret_cast<uint32_t *>(&B0[ml * 16 + chunk]) + (lk * 2);
+                dst[0] = pack2<DT>(v[0], v[1]);
+                dst[1] = pack2<DT>(v[2], v[3]);
+            }
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int p = 0; p < BM / 32; ++p) {
+            const int row = p * 32 + (tid >> 4), ch = tid & 15;
+            const int m = m0 + row, n = n0 + ch * 8;
+            const u32x4 v = B0[row * 16 + (ch ^ (row & 15))];
+            if (m >= M || n >= N)
+                continue;
+            uint16_t *dst = y + (int64_t)m * N + n;
+            if (vec_out && n + 8 <= N) {
+                *reinterpret_cast<u32x4 *>(dst) = v;
+            } else {
+                const int cnt = min(8, N - n);
+                for (int e = 0; e < cnt; ++e)
+                    dst[e] = (uint16_t)((v[e >> 1] >> ((e & 1) * 16)) & 0xffffu);
+            }
+        }
+        return;
+    }
     // ---- epilogue: bias + activation in registers, staged row-major in
     // LDS (rows 0-63 in B0, 64-127 in B1; 16-byte chunks XOR-swizzled by
     // row), then written with 128-bit stores
@@ -713,7 +778,7 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
     }
 }
 
-template <int DT, int STATS, int GB, bool KT, bool LN>
+template <int DT, int STATS, int GB, bool KT, bool LN, bool GT>
 hipError_t launch_k(const GemmArgs &a, hipStream_t s)
 {
     int dev = 0, cus = 256;
@@ -721,69 +786,84 @@ hipError_t launch_k(const GemmArgs &a, hipStream_t s)
         (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (cus < 1)
         cus = 256;
+    constexpr int BNO = GT ? BN / 2 : BN;
     TileMap mp;
     mp.tm = (int)((a.M + BM - 1) / BM);
-    mp.tn = (int)((a.N + BN - 1) / BN);
+    mp.tn = (int)((a.N + BNO - 1) / BNO);
     mp.T = mp.tm * mp.tn;
     mp.xcd = (cus % 8 == 0 && mp.tn % 8 == 0) ? 1 : 0;
     const int vec_out = (a.N % 8 == 0 && ((uintptr_t)a.y & 15u) == 0) ? 1 : 0;
     if constexpr (STATS == ST_FROM_Y) {
         hipLaunchKernelGGL((row_stats_to_y_kernel<DT>), dim3((unsigned)((a.M + 3) / 4)), dim3(256),
                            0, s, (const uint16_t *)a.x, (uint16_t *)a.y, (int)a.M, (int)a.N,
-                           (int)a.K, a.eps, a.norm, mp.tn);
+                           (int)a.K, a.eps, a.norm, mp.tn, BNO);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
     }
-    hipLaunchKernelGGL((prefill_lds_kernel<DT, STATS, GB, KT, LN>), dim3(mp.T), dim3(THREADS), 0, s,
+    hipLaunchKernelGGL((prefill_lds_kernel<DT, STATS, GB, KT, LN, GT>), dim3(mp.T), dim3(THREADS), 0, s,
                        (const uint16_t *)a.x, (const uint16_t *)a.gamma, (const uint16_t *)a.beta,
                        (const uint16_t *)a.W, (const uint16_t *)a.bias, (uint16_t *)a.y, (int)a.M,
                        (int)a.N, (int)a.K, a.eps, a.norm, a.act, mp, vec_out);
     return hipGetLastError();
 }
 
-template <int DT, int STATS, int GB, bool LN>
+template <int DT, int STATS, int GB, bool LN, bool GT>
 hipError_t launch_t(const GemmArgs &a, hipStream_t s)
 {
-    return a.K % BK ? launch_k<DT, STATS, GB, true, LN>(a, s)
-                    : launch_k<DT, STATS, GB, false, LN>(a, s);
+    return a.K % BK ? launch_k<DT, STATS, GB, true, LN, GT>(a, s)
+                    : launch_k<DT, STATS, GB, false, LN, GT>(a, s);
 }
 
-template <int DT, int STATS, bool LN>
+template <int DT, int STATS, bool LN, bool GT>
 hipError_t launch_gb(const GemmArgs &a, hipStream_t s)
 {
     switch ((a.gamma ? 1 : 0) | (a.beta ? 2 : 0)) {
-    case 0: return launch_t<DT, STATS, 0, LN>(a, s);
-    case 1: return launch_t<DT, STATS, 1, LN>(a, s);
-    case 2: return launch_t<DT, STATS, 2, LN>(a, s);
-    default: return launch_t<DT, STATS, 3, LN>(a, s);
+    case 0: return launch_t<DT, STATS, 0, LN, GT>(a, s);
+    case 1: return launch_t<DT, STATS, 1, LN, GT>(a, s);
+    case 2: return launch_t<DT, STATS, 2, LN, GT>(a, s);
+    default: return launch_t<DT, STATS, 3, LN, GT>(a, s);
     }
 }
 
-template <int DT, int STATS>
+template <int DT, int STATS, bool GT>
 hipError_t launch_norm(const GemmArgs &a, hipStream_t s)
 {
-    return a.norm == NORM_LAYERNORM ? launch_gb<DT, STATS, true>(a, s)
-                                    : launch_gb<DT, STATS, false>(a, s);
+    return a.norm == NORM_LAYERNORM ? launch_gb<DT, STATS, true, GT>(a, s)
+                                    : launch_gb<DT, STATS, false, GT>(a, s);
 }
 
-template <int DT>
+template <int DT, bool GT>
 hipError_t launch_dt(const GemmArgs &a, hipStream_t s)
 {
     if (a.norm == NORM_NONE)
-        return launch_t<DT, ST_NONE, 0, false>(a, s);
+        return launch_t<DT, ST_NONE, 0, false, GT>(a, s);
     // The statistics pass needs 8 bytes of y in every tile's rows: every
     // tile (including the last, partial one) must have at least 4 columns
     // and the rows must be 8-byte aligned.
     const bool y_scratch = a.N % 8 == 0 && ((uintptr_t)a.y & 15u) == 0 && !stats_in_kernel();
-    return y_scratch ? launch_norm<DT, ST_FROM_Y>(a, s) : launch_norm<DT, ST_PROLOGUE>(a, s);
+    return y_scratch ? launch_norm<DT, ST_FROM_Y, GT>(a, s) : launch_norm<DT, ST_PROLOGUE, GT>(a, s);
 }
 
 }  // namespace
 
 hipError_t launch_prefill_lds(const GemmArgs &a, hipStream_t s)
 {
-    return a.dtype == DT_F16 ? launch_dt<DT_F16>(a, s) : launch_dt<DT_BF16>(a, s);
+    return a.dtype == DT_F16 ? launch_dt<DT_F16, false>(a, s) : launch_dt<DT_BF16, false>(a, s);
+}
+
+bool prefill_gated_fits(const GemmArgs &a)
+{
+    // W row offsets within a tile (up to N + 127 rows past its first gate
+    // row) are 32-bit byte offsets
+    return a.vec && a.M > kDecodeMaxM && (a.N + BN) * a.K * 2 <= (int64_t)UINT32_MAX;
+}
+
+hipError_t launch_prefill_lds_gated(const GemmArgs &a, hipStream_t s)
+{
+    if (!prefill_gated_fits(a))
+        return hipErrorInvalidValue;
+    return a.dtype == DT_F16 ? launch_dt<DT_F16, true>(a, s) : launch_dt<DT_BF16, true>(a, s);
 }
 
 }  // namespace ng

@@ -78,12 +78,61 @@ int ng_validate_gemm(const void *x, const void *gamma, const void *beta, const v
     return NG_OK;
 }
 
+/* Workspace elements per M * F: h, plus [gate | up] of every row when gated. */
+static size_t ffn_workspace(int64_t M, int64_t F, int dtype, int per)
+{
+    if (M < 1 || F < 1 || (dtype != NG_DTYPE_F16 && dtype != NG_DTYPE_BF16) ||
+        !mul_ok(M, F * per))
+        return 0;
+    size_t bytes = (size_t)M * (size_t)F * (size_t)per * 2u;
+    return (bytes + 255u) & ~(size_t)255u;
+}
+
 size_t ng_ffn_workspace_size(int64_t M, int64_t F, int dtype)
 {
-    if (M < 1 || F < 1 || (dtype != NG_DTYPE_F16 && dtype != NG_DTYPE_BF16) || !mul_ok(M, F))
-        return 0;
-    size_t bytes = (size_t)M * (size_t)F * 2u;
-    return (bytes + 255u) & ~(size_t)255u;
+    return ffn_workspace(M, F, dtype, 1);
+}
+
+size_t ng_gated_ffn_workspace_size(int64_t M, int64_t F, int dtype)
+{
+    return F <= NG_MAX_DIM / 2 ? ffn_workspace(M, F, dtype, 3) : 0;
+}
+
+/* gated: W1 is [2F, K] and b1 [2F]; the workspace holds 3 M F elements. */
+static int validate_ffn(const void *x, const void *gamma, const void *beta, const void *W1,
+                        const void *b1, const void *W2, const void *b2, const void *y,
+                        int64_t M, int64_t K, int64_t F, int64_t N, float eps, int norm,
+                        int act, int dtype, const void *workspace, size_t workspace_bytes,
+                        int gated)
+{
+    const int64_t F1 = gated ? 2 * F : F;     /* rows of W1 */
+    if (!x || !W1 || !W2 || !y)
+        return NG_ERR_NULL;
+    if (!enums_ok(norm, act, dtype))
+        return NG_ERR_ENUM;
+    if (!dim_ok(M) || !dim_ok(K) || !dim_ok(F) || !dim_ok(N) || (gated && F > NG_MAX_DIM / 2) ||
+        !mul_ok(M, K) || !mul_ok(F1, K) || !mul_ok(N, F) || !mul_ok(M, F1 + F) || !mul_ok(M, N))
+        return NG_ERR_SHAPE;
+    if (!eps_ok(eps, norm))
+        return NG_ERR_EPS;
+    if (!align2(x) || !align2(gamma) || !align2(beta) || !align2(W1) || !align2(b1) ||
+        !align2(W2) || !align2(b2) || !align2(y) || !align2(workspace))
+        return NG_ERR_ALIGN;
+    range_t in[7] = {rng(x, M * K), rng(gamma, K), rng(beta, K), rng(W1, F1 * K),
+                     rng(b1, F1),   rng(W2, N * F), rng(b2, N)};
+    range_t ry = rng(y, M * N);
+    for (int i = 0; i < 7; ++i)
+        if (overlap(ry, in[i]))
+            return NG_ERR_ALIAS;
+    if (!workspace || workspace_bytes < ffn_workspace(M, F, dtype, gated ? 3 : 1))
+        return NG_ERR_WORKSPACE;
+    range_t rw = rng(workspace, M * F * (gated ? 3 : 1));
+    if (overlap(rw, ry))
+        return NG_ERR_ALIAS;
+    for (int i = 0; i < 7; ++i)
+        if (overlap(rw, in[i]))
+            return NG_ERR_ALIAS;
+    return NG_OK;
 }
 
 int ng_validate_ffn(const void *x, const void *gamma, const void *beta, const void *W1,
@@ -91,33 +140,17 @@ int ng_validate_ffn(const void *x, const void *gamma, const void *beta, const vo
                     int64_t M, int64_t K, int64_t F, int64_t N, float eps, int norm, int act,
                     int dtype, const void *workspace, size_t workspace_bytes)
 {
-    if (!x || !W1 || !W2 || !y)
-        return NG_ERR_NULL;
-    if (!enums_ok(norm, act, dtype))
-        return NG_ERR_ENUM;
-    if (!dim_ok(M) || !dim_ok(K) || !dim_ok(F) || !dim_ok(N) || !mul_ok(M, K) ||
-        !mul_ok(F, K) || !mul_ok(N, F) || !mul_ok(M, F) || !mul_ok(M, N))
-        return NG_ERR_SHAPE;
-    if (!eps_ok(eps, norm))
-        return NG_ERR_EPS;
-    if (!align2(x) || !align2(gamma) || !align2(beta) || !align2(W1) || !align2(b1) ||
-        !align2(W2) || !align2(b2) || !align2(y) || !align2(workspace))
-        return NG_ERR_ALIGN;
-    range_t in[7] = {rng(x, M * K), rng(gamma, K), rng(beta, K), rng(W1, F * K),
-                     rng(b1, F),    rng(W2, N * F), rng(b2, N)};
-    range_t ry = rng(y, M * N);
-    for (int i = 0; i < 7; ++i)
-        if (overlap(ry, in[i]))
-            return NG_ERR_ALIAS;
-    if (!workspace || workspace_bytes < ng_ffn_workspace_size(M, F, dtype))
-        return NG_ERR_WORKSPACE;
-    range_t rw = rng(workspace, M * F);
-    if (overlap(rw, ry))
-        return NG_ERR_ALIAS;
-    for (int i = 0; i < 7; ++i)
-        if (overlap(rw, in[i]))
-            return NG_ERR_ALIAS;
-    return NG_OK;
+    return validate_ffn(x, gamma, beta, W1, b1, W2, b2, y, M, K, F, N, eps, norm, act, dtype,
+                        workspace, workspace_bytes, 0);
+}
+
+int ng_validate_gated_ffn(const void *x, const void *gamma, const void *beta, const void *W1,
+                          const void *b1, const void *W2, const void *b2, const void *y,
+                          int64_t M, int64_t K, int64_t F, int64_t N, float eps, int norm,
+                          int act, int dtype, const void *workspace, size_t workspace_bytes)
+{
+    return validate_ffn(x, gamma, beta, W1, b1, W2, b2, y, M, K, F, N, eps, norm, act, dtype,
+                        workspace, workspace_bytes, 1);
 }
 
 int ng_vector_ok(int64_t K, const void *a, const void *b, const void *c, const void *d)

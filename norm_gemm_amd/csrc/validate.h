@@ -21,10 +21,17 @@ int ng_validate_ffn(const void *x, const void *gamma, const void *beta, const vo
                     int64_t M, int64_t K, int64_t F, int64_t N, float eps, int norm, int act,
                     int dtype, const void *workspace, size_t workspace_bytes);
 
+/* As ng_validate_ffn with W1 [2F, K], b1 [2F] and a 3 M F workspace. */
+int ng_validate_gated_ffn(const void *x, const void *gamma, const void *beta, const void *W1,
+                          const void *b1, const void *W2, const void *b2, const void *y,
+                          int64_t M, int64_t K, int64_t F, int64_t N, float eps, int norm,
+                          int act, int dtype, const void *workspace, size_t workspace_bytes);
+
 /* 1 when every given pointer is 16-byte aligned and K % 8 == 0. */
 int ng_vector_ok(int64_t K, const void *a, const void *b, const void *c, const void *d);
 
 size_t ng_ffn_workspace_size(int64_t M, int64_t F, int dtype);
+size_t ng_gated_ffn_workspace_size(int64_t M, int64_t F, int dtype);
 
 #ifdef __cplusplus
 }

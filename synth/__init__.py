@@ -170,6 +170,13 @@ def ffn_silu_512x14336x49152(seed: int = 0) -> Case:
                     49152, 14336, act=ACT_SILU, seed=seed)
 
 
+def gated_ffn_swiglu_512x8192x28672(seed: int = 0) -> Case:
+    """RMSNorm -> [gate; up] -> SiLU(gate) * up -> down, LLaMA-2-70B FFN sizes."""
+    return make_gated_ffn("gated_ffn_swiglu_rms_x512x8192_w1_57344_w2_8192_f16", 512, 8192,
+                          28672, 8192, norm=NORM_RMSNORM, act=ACT_SILU, eps=1e-5, gamma=True,
+                          seed=seed)
+
+
 def decode_rms_gemm_8192x28672(M: int, seed: int = 0) -> Case:
     return make_norm_gemm(f"decode_rms_gemm_m{M}_x{M}x8192_w28672x8192_bf16", M,
                           8192, 28672, dtype=BF16, norm=NORM_RMSNORM,
@@ -181,6 +188,7 @@ WORKLOADS = {
     "ln_linear_bias_1024x8192": ln_linear_bias_1024x8192,
     "rms_matmul_silu_512x14336": rms_matmul_silu_512x14336,
     "ffn_silu_512x14336x49152": ffn_silu_512x14336x49152,
+    "gated_ffn_swiglu_512x8192x28672": gated_ffn_swiglu_512x8192x28672,
     "decode_rms_gemm_m1": lambda seed=0: decode_rms_gemm_8192x28672(1, seed),
     "decode_rms_gemm_m8": lambda seed=0: decode_rms_gemm_8192x28672(8, seed),
     "decode_rms_gemm_m32": lambda seed=0: decode_rms_gemm_8192x28672(32, seed),

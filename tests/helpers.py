@@ -47,6 +47,9 @@ def run_case_gpu(case, device="cuda"):
     up = lambda k: upload(A.get(k), case.dtype, device)
     norm = case.norm
     act = case.act
+    if case.kind == "gated_ffn":
+        return ng.fused_gated_ffn(up("x"), up("W1"), up("W2"), up("gamma"), up("beta"), up("b1"),
+                                  up("b2"), eps=case.eps, norm=norm, act=act)
     if case.kind == "ffn":
         return ng.fused_ffn(up("x"), up("W1"), up("W2"), up("gamma"), up("beta"), up("b1"),
                             up("b2"), eps=case.eps, norm=norm, act=act)

@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert ng.norm_gemm_abi_version() == 2
+    assert ng.norm_gemm_abi_version() == 3
     for s in (OK, NULL, SHAPE, ENUM, EPS, ALIAS, WORKSPACE, UNSUP, ALIGN, HIP):
         assert ng.norm_gemm_status_string(s)
     assert ng.norm_gemm_status_string(12345) == "unknown status"
@@ -103,6 +103,33 @@ def ffn(x=X, g=G, b=B, w1=W, b1=BI, w2=0x90000000, b2=0xA0000000, y=Y, M=4, K=16
 @no_gpu_only
 def test_fused_ffn_validation_errors(kw, status):
     assert ffn(**kw) == status
+
+
+def gffn(x=X, g=G, b=B, w1=W, b1=BI, w2=0x90000000, b2=0xA0000000, y=Y, M=4, K=16, F=32, N=8,
+         eps=1e-5, norm=1, act=1, dtype=0, ws=WS, wsb=3 * 4 * 32 * 2):
+    return ng.lib.fused_gated_ffn(x, g, b, w1, b1, w2, b2, y, M, K, F, N, eps, norm, act, dtype,
+                                  ws, wsb, None)
+
+
+def test_gated_ffn_workspace_size():
+    assert ng.fused_gated_ffn_workspace_size(512, 28672, 0) == 3 * 512 * 28672 * 2
+    assert ng.fused_gated_ffn_workspace_size(3, 5, 1) == 256
+    assert ng.fused_gated_ffn_workspace_size(0, 5, 0) == 0
+    assert ng.fused_gated_ffn_workspace_size(3, 5, 7) == 0
+    assert ng.fused_gated_ffn_workspace_size(1, 2 ** 30, 0) == 0
+
+
+# W1 is [2F, K] (2 KB here) and b1 [2F]: overlaps with their second halves
+# are caught; the workspace must hold 3 M F elements.
+@pytest.mark.parametrize("kw,status", [
+    (dict(w1=None), NULL), (dict(act=9), ENUM), (dict(F=0), SHAPE), (dict(F=2 ** 30), SHAPE),
+    (dict(wsb=3 * 4 * 32 * 2 - 1), WORKSPACE), (dict(wsb=4 * 32 * 2), WORKSPACE),
+    (dict(y=W + 2 * 32 * 16 * 2 - 64), ALIAS), (dict(y=BI + 2 * 32 * 2 - 2), ALIAS),
+    (dict(ws=W + 2 * 32 * 16 * 2 - 256), ALIAS), (dict(ws=Y - 512), ALIAS),
+])
+@no_gpu_only
+def test_fused_gated_ffn_validation_errors(kw, status):
+    assert gffn(**kw) == status
 
 
 def test_python_binding_rejects_cpu_tensors():

@@ -346,6 +346,54 @@ def test_ffn_chain_norm_bias_act(M, K, F, N, norm, act):
     check_full(case)
 
 
+# Gated (SwiGLU-style) FFN: tiles that hold the gate and up rows of the same
+# columns (M > 32, aligned; ragged M, F and K; F % 8 != 0 takes the in-kernel
+# statistics; several row and column blocks, XCD-grouped), and the
+# projections + gating kernel path (M <= 32, K % 8 != 0).
+GATED_SHAPES = [
+    (70, 136, 200, 72, LN, SILU, F16),
+    (129, 264, 384, 136, RMS, SILU, F16),
+    (257, 520, 1000, 256, NONE, GELU, BF16),
+    (200, 64, 130, 40, LN, RELU, F16),
+    (300, 1024, 2048, 512, RMS, SILU, F16),
+    (16, 128, 320, 96, RMS, SILU, BF16),
+    (5, 264, 136, 48, NONE, GELU, F16),
+    (33, 37, 50, 20, LN, SILU, F16),
+]
+
+
+@pytest.mark.parametrize("M,K,F,N,norm,act,dtype", GATED_SHAPES)
+def test_gated_ffn(M, K, F, N, norm, act, dtype):
+    case = synth.make_gated_ffn(f"gated_ffn_{M}x{K}x{F}x{N}_n{norm}a{act}d{dtype}", M, K, F, N,
+                                dtype=dtype, norm=norm, act=act, gamma=norm != NONE,
+                                beta=norm == LN, b1=True, b2=True, seed=M + K + F + N)
+    check_full(case)
+
+
+@pytest.mark.parametrize("M", [8, 100])
+def test_stacked_qkv_weight_equals_three_calls(M):
+    """One RMSNorm output feeding the Q, K and V projections (grouped K/V
+    heads) through one call on the stacked [Wq; Wk; Wv] weight: equal to the
+    three separate calls, bit for bit on the tiled path (the arithmetic of an
+    output element does not depend on N), within tolerance of the oracle."""
+    import norm_gemm_amd as ng
+    K, NQ, NKV = 512, 512, 128
+    case = synth.make_norm_gemm(f"qkv_{M}", M, K, NQ + 2 * NKV, norm=RMS, beta=False,
+                                bias=False, eps=1e-5, seed=21 + M)
+    A = case.arrays
+    x, g, W = upload(A["x"], F16), upload(A["gamma"], F16), upload(A["W"], F16)
+    y = ng.fused_norm_gemm(x, W, g, eps=1e-5, norm=RMS)
+    parts = [ng.fused_norm_gemm(x, W[a:b].contiguous(), g, eps=1e-5, norm=RMS)
+             for a, b in ((0, NQ), (NQ, NQ + NKV), (NQ + NKV, NQ + 2 * NKV))]
+    torch.cuda.synchronize()
+    joined = torch.cat(parts, dim=1)
+    assert_close(to_f64(y), oracle.run_case(case), what="stacked qkv")
+    if M > 32:
+        assert torch.equal(y.view(torch.int16), joined.view(torch.int16))
+    else:
+        assert_close(to_f64(joined), to_f64(y), tol=2e-3, what="qkv parts")
+
+
 @pytest.mark.parametrize("M", [16, 100])
 def test_ffn_equals_two_norm_gemm_calls(M):
     import norm_gemm_amd as ng
@@ -394,6 +442,12 @@ def test_ffn_chain_ln_relu_bias_1024x8192():
                           8192, norm=LN, act=RELU, gamma=True, beta=True, b1=True, b2=True,
                           seed=0)
     check_sampled(case, 4, 300)
+
+
+def test_gated_ffn_swiglu_rms_512x8192x28672():
+    """SwiGLU FFN of the LLaMA-2-70B layer: RMSNorm, [gate; up] 2 x 28672 x 8192,
+    down 8192 x 28672, fp16."""
+    check_sampled(synth.gated_ffn_swiglu_512x8192x28672(), 3, 200)
 
 
 @pytest.mark.parametrize("M", [1, 8, 32])
