@@ -96,6 +96,12 @@ int fused_norm_gemm(const void *x, const void *gamma, const void *beta,
  *
  * h lives in the caller-provided workspace (device memory of at least
  * fused_ffn_workspace_size(M, F, dtype) bytes, 256-byte aligned recommended).
+ * A workspace of at least fused_ffn_workspace_size(M, F, dtype) + 8 M N bytes
+ * also holds two fp32 partial sums of y: when the second GEMM's 128 x 256
+ * tiles fill at most half of the compute units (and M > 32, aligned), its K
+ * is then split over two workgroups per tile and the partials are added in a
+ * fixed order (deterministic) by a second kernel. Every workspace byte the
+ * call may touch is checked against the inputs and y (NG_ERR_ALIAS).
  * Two kernel launches on `stream`, in order. The workspace must not overlap
  * any input or y; it may be reused once the call's work has completed on the
  * stream. Returns an ng_status_t.
@@ -125,7 +131,9 @@ int fused_ffn(const void *x, const void *gamma, const void *beta,
  * the [gate | up] projections of every row go to the workspace and a second
  * kernel forms h. The workspace must hold fused_gated_ffn_workspace_size(M,
  * F, dtype) bytes (3 M F elements: h, then the [M, 2F] projections); other
- * conventions as fused_ffn. Returns an ng_status_t.
+ * conventions as fused_ffn, including the split K of the second GEMM, whose
+ * partials (8 M N bytes after the 256-byte-rounded h) fit in this size when
+ * 2 N <= F, up to that rounding. Returns an ng_status_t.
  */
 size_t fused_gated_ffn_workspace_size(int64_t M, int64_t F, int dtype);
 

@@ -44,6 +44,33 @@ int run(const ng::GemmArgs &a, hipStream_t s)
     return e == hipSuccess ? NG_OK : NG_ERR_HIP;
 }
 
+// Second GEMM of an FFN: y = h . W2^T + b2. When its tiles fill at most
+// half of the CUs and the workspace past h holds two fp32 partial sums of y,
+// K is split over two workgroups per tile and the partials are added in a
+// fixed order by a second kernel.
+int ffn_down(const void *h, const void *W2, const void *b2, void *y, int64_t M, int64_t F,
+             int64_t N, int dtype, void *workspace, size_t workspace_bytes, hipStream_t s)
+{
+    const ng::GemmArgs a = make_args(h, nullptr, nullptr, W2, b2, y, M, N, F, 0.0f,
+                                     NG_NORM_NONE, NG_ACT_NONE, dtype);
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) == hipSuccess)
+        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const size_t hbytes = (((size_t)M * (size_t)F * 2u) + 255u) & ~(size_t)255u;
+    const size_t pbytes = 2u * (size_t)M * (size_t)N * 4u;
+    char *part = (char *)workspace + hbytes;
+    if (a.vec && M > ng::kDecodeMaxM && cus > 0 && 2 * ng::prefill_tiles(M, N) <= cus &&
+        ng::prefill_k_steps(F) >= 4 && workspace_bytes >= hbytes + pbytes &&
+        ((uintptr_t)part & 15u) == 0) {
+        if (ng::launch_prefill_lds_splitk(a, (float *)part, 2, s) != hipSuccess ||
+            ng::launch_splitk_sum((const float *)part, b2, y, M, N, 2, NG_ACT_NONE, dtype, s) !=
+                hipSuccess)
+            return NG_ERR_HIP;
+        return NG_OK;
+    }
+    return run(a, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -79,9 +106,7 @@ int fused_ffn(const void *x, const void *gamma, const void *beta, const void *W1
     if (st != NG_OK)
         return st;
     // phase 2: y = h . W2^T + b2
-    return run(make_args(workspace, nullptr, nullptr, W2, b2, y, M, N, F, 0.0f, NG_NORM_NONE,
-                         NG_ACT_NONE, dtype),
-               s);
+    return ffn_down(workspace, W2, b2, y, M, F, N, dtype, workspace, workspace_bytes, s);
 }
 
 size_t fused_gated_ffn_workspace_size(int64_t M, int64_t F, int dtype)
@@ -116,10 +141,8 @@ int fused_gated_ffn(const void *x, const void *gamma, const void *beta, const vo
         if (ng::launch_gate(gu, h, M, F, act, dtype, s) != hipSuccess)
             return NG_ERR_HIP;
     }
-    // phase 2: y = h . W2^T + b2
-    return run(make_args(h, nullptr, nullptr, W2, b2, y, M, N, F, 0.0f, NG_NORM_NONE,
-                         NG_ACT_NONE, dtype),
-               s);
+    // phase 2: y = h . W2^T + b2 (the [gate | up] area is free by now)
+    return ffn_down(h, W2, b2, y, M, F, N, dtype, workspace, workspace_bytes, s);
 }
 
 const char *norm_gemm_status_string(int status)

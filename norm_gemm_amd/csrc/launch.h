@@ -25,6 +25,13 @@ bool decode_wide_fits(const GemmArgs &a);  // M <= 16, N >= 16, 32-bit slab offs
 // gated tiled kernel: a.W = [W_gate; W_up] is [2 a.N, a.K], a.bias [2 a.N]
 bool prefill_gated_fits(const GemmArgs &a);  // a.vec, M > 32, 32-bit W row offsets
 hipError_t launch_prefill_lds_gated(const GemmArgs &a, hipStream_t s);
+// split K of the plain tiled GEMM (a.vec, no normalization): fp32 partials
+// part[ksplit][M][N], then y = act(sum of the partials + bias)
+int prefill_tiles(int64_t M, int64_t N);
+int prefill_k_steps(int64_t K);
+hipError_t launch_prefill_lds_splitk(const GemmArgs &a, float *part, int ksplit, hipStream_t s);
+hipError_t launch_splitk_sum(const float *part, const void *bias, void *y, int64_t M, int64_t N,
+                             int ksplit, int act, int dtype, hipStream_t s);
 // h[M, F] = act(gu[:, :F]) * gu[:, F:] for gu[M, 2F]
 hipError_t launch_gate(const void *gu, void *h, int64_t M, int64_t F, int act, int dtype,
                        hipStream_t s);

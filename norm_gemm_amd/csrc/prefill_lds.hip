@@ -173,14 +173,19 @@ __global__ __launch_bounds__(256) void row_stats_to_y_kernel(const uint16_t *__r
 // GB: bit 0 gamma present, bit 1 beta present (with STATS != ST_NONE);
 // KT: K % 64 != 0 (the last K step is ragged); LN: LayerNorm (else RMSNorm,
 // with STATS != ST_NONE); GT: gated output (see the gated epilogue): W is
-// [2N, K] = [W_gate; W_up], bias [2N], and a tile covers 128 output columns.
-template <int DT, int STATS, int GB, bool KT, bool LN, bool GT>
+// [2N, K] = [W_gate; W_up], bias [2N], and a tile covers 128 output columns;
+// SK: split K (no normalization): workgroup b computes tile b % T over the
+// b / T-th of ksplit contiguous K ranges and writes its fp32 partial sums to
+// part[b / T][M][N] (bias and activation are applied by the sum of the
+// partials).
+template <int DT, int STATS, int GB, bool KT, bool LN, bool GT, bool SK>
 __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ gamma,
     const uint16_t *__restrict__ beta, const uint16_t *__restrict__ W,
     const uint16_t *__restrict__ bias, uint16_t *__restrict__ y, int M, int N, int K,
-    float eps, int norm, int act, TileMap mp, int vec_out)
+    float eps, int norm, int act, TileMap mp, int vec_out, float *__restrict__ part, int ksplit)
 {
+    static_assert(!SK || (STATS == ST_NONE && !GT), "split K only for the plain GEMM");
     constexpr bool AFFINE = STATS != ST_NONE;
     constexpr bool HG = AFFINE && (GB & 1), HB = AFFINE && (GB & 2);
     // direct loads per lane per K step: W, plus x when it is not normalized
@@ -216,14 +221,21 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WGN, wn = wave % WGN;
     const int lrow = lane & 31, lk = lane >> 5;
-    const int nk = (K + BK - 1) / BK;
+    // K range of this workgroup: all of K, or with split K the ks-th of
+    // ksplit ranges of whole K steps (the host gives every range a step).
+    // Ke is the extent of the range; K stays the row stride.
+    const int ks = SK ? (int)blockIdx.x / mp.T : 0;
+    const int nks = SK ? ((K + BK - 1) / BK + ksplit - 1) / ksplit : 0;
+    const int kbase = SK ? ks * nks * BK : 0;
+    const int Ke = SK ? min(K - kbase, nks * BK) : K;
+    const int nk = (Ke + BK - 1) / BK;
     constexpr bool k_tail = KT;
 
     // output columns per tile: 256, or 128 gated (the 256 W rows of a tile are
     // the gate and up rows of the same 128 columns)
     constexpr int BNO = GT ? BN / 2 : BN;
     int mb, nt;
-    tile_of(mp, blockIdx.x, mb, nt);
+    tile_of(mp, SK ? (int)blockIdx.x % mp.T : (int)blockIdx.x, mb, nt);
     const int m0 = mb * BM, n0 = nt * BNO;
 
     // ---- direct HBM -> LDS loads. Instruction i of a wave fills 8 tile rows
@@ -239,13 +251,13 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
     // of a ragged K has its own fixed offsets: chunks past K re-read the
     // row's last valid chunk (in bounds) and are zeroed once landed.
     const int kl = (nk - 1) * BK;                     // first k of the last step
-    const int clast = (K - kl + 7) / 8 - 1;           // last valid chunk in it
-    auto tail_chunk = [&](int c) { return kl + c * 8 < K ? c : clast; };
+    const int clast = (Ke - kl + 7) / 8 - 1;          // last valid chunk in it
+    auto tail_chunk = [&](int c) { return kl + c * 8 < Ke ? c : clast; };
     int wch[B_DMA], ach[A_DMA];
     uint32_t woff[B_DMA], woff_t[B_DMA], aoff_g[A_DMA], aoff_t[A_DMA];
     bool alive[A_DMA];
-    const uint16_t *wtile = W + (int64_t)n0 * K;
-    const uint16_t *xtile = x + (int64_t)m0 * K;
+    const uint16_t *wtile = W + (int64_t)n0 * K + kbase;
+    const uint16_t *xtile = x + (int64_t)m0 * K + kbase;
 #pragma unroll
     for (int i = 0; i < B_DMA; ++i) {
         const int row = wave * B_RPW + i * 8 + (lane >> 3);
@@ -468,7 +480,7 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
     // without normalization only the chunks past K of the last step need
     // zeroing (rows past M re-read row M - 1 and their outputs are dropped)
     auto zero_tail_x = [&](u32x4 *As) {
-        if ((nk - 1) * BK + ach[0] * 8 >= K) {
+        if ((nk - 1) * BK + ach[0] * 8 >= Ke) {
 #pragma unroll
             for (int i = 0; i < A_DMA; ++i)
                 As[(i * A_IST + wave * 8) * CPR + lane] = u32x4{0u, 0u, 0u, 0u};
@@ -478,7 +490,7 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
 #pragma unroll
         for (int i = 0; i < B_DMA; ++i) {
             const int row = wave * B_RPW + i * 8 + (lane >> 3);
-            if ((nk - 1) * BK + wch[i] * 8 >= K)
+            if ((nk - 1) * BK + wch[i] * 8 >= Ke)
                 Bs[row * CPR + (lane & 7)] = u32x4{0u, 0u, 0u, 0u};
         }
     };
@@ -675,6 +687,33 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
     wait_vmcnt<0>();
     __syncthreads();
 
+    if constexpr (SK) {
+        // ---- split-K epilogue: fp32 partials straight from the accumulators,
+        // four consecutive columns (16 bytes) per lane and 32x32 block row
+        float *pp = part + (size_t)ks * M * N;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int n = n0 + wn * WN + j * 32 + q * 8 + lk * 4;
+#pragma unroll
+                for (int i = 0; i < FM; ++i) {
+                    const int m = m0 + wm * WM + i * 32 + lrow;
+                    if (m >= M || n >= N)
+                        continue;
+                    float *dst = pp + (size_t)m * N + n;
+                    if (n + 4 <= N && (N & 3) == 0) {
+                        *reinterpret_cast<floatx4 *>(dst) =
+                            floatx4{acc[j][i][q * 4], acc[j][i][q * 4 + 1], acc[j][i][q * 4 + 2],
+                                    acc[j][i][q * 4 + 3]};
+                    } else {
+                        for (int r = 0; r < 4 && n + r < N; ++r)
+                            dst[r] = acc[j][i][q * 4 + r];
+                    }
+                }
+            }
+        return;
+    }
     if constexpr (GT) {
         // ---- gated epilogue: each lane holds the gate (j = 0) and up (j = 1)
         // sums of the same output elements; h = act(gate + b_gate) *
@@ -778,8 +817,8 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
     }
 }
 
-template <int DT, int STATS, int GB, bool KT, bool LN, bool GT>
-hipError_t launch_k(const GemmArgs &a, hipStream_t s)
+template <int DT, int STATS, int GB, bool KT, bool LN, bool GT, bool SK = false>
+hipError_t launch_k(const GemmArgs &a, hipStream_t s, float *part = nullptr, int ksplit = 1)
 {
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess)
@@ -801,10 +840,11 @@ hipError_t launch_k(const GemmArgs &a, hipStream_t s)
         if (e != hipSuccess)
             return e;
     }
-    hipLaunchKernelGGL((prefill_lds_kernel<DT, STATS, GB, KT, LN, GT>), dim3(mp.T), dim3(THREADS), 0, s,
+    hipLaunchKernelGGL((prefill_lds_kernel<DT, STATS, GB, KT, LN, GT, SK>), dim3(mp.T * ksplit),
+                       dim3(THREADS), 0, s,
                        (const uint16_t *)a.x, (const uint16_t *)a.gamma, (const uint16_t *)a.beta,
                        (const uint16_t *)a.W, (const uint16_t *)a.bias, (uint16_t *)a.y, (int)a.M,
-                       (int)a.N, (int)a.K, a.eps, a.norm, a.act, mp, vec_out);
+                       (int)a.N, (int)a.K, a.eps, a.norm, a.act, mp, vec_out, part, ksplit);
     return hipGetLastError();
 }
 
@@ -857,6 +897,30 @@ bool prefill_gated_fits(const GemmArgs &a)
     // W row offsets within a tile (up to N + 127 rows past its first gate
     // row) are 32-bit byte offsets
     return a.vec && a.M > kDecodeMaxM && (a.N + BN) * a.K * 2 <= (int64_t)UINT32_MAX;
+}
+
+int prefill_tiles(int64_t M, int64_t N)
+{
+    return (int)(((M + BM - 1) / BM) * ((N + BN - 1) / BN));
+}
+
+int prefill_k_steps(int64_t K)
+{
+    return (int)((K + BK - 1) / BK);
+}
+
+hipError_t launch_prefill_lds_splitk(const GemmArgs &a, float *part, int ksplit,
+                                     hipStream_t s)
+{
+    // plain GEMM only; every K range must get at least one step
+    if (!a.vec || a.norm != NORM_NONE || ksplit < 2 || prefill_k_steps(a.K) < 2 * ksplit)
+        return hipErrorInvalidValue;
+    const bool kt = a.K % BK != 0;
+    if (a.dtype == DT_F16)
+        return kt ? launch_k<DT_F16, ST_NONE, 0, true, false, false, true>(a, s, part, ksplit)
+                  : launch_k<DT_F16, ST_NONE, 0, false, false, false, true>(a, s, part, ksplit);
+    return kt ? launch_k<DT_BF16, ST_NONE, 0, true, false, false, true>(a, s, part, ksplit)
+              : launch_k<DT_BF16, ST_NONE, 0, false, false, false, true>(a, s, part, ksplit);
 }
 
 hipError_t launch_prefill_lds_gated(const GemmArgs &a, hipStream_t s)

@@ -124,9 +124,21 @@ static int validate_ffn(const void *x, const void *gamma, const void *beta, cons
     for (int i = 0; i < 7; ++i)
         if (overlap(ry, in[i]))
             return NG_ERR_ALIAS;
-    if (!workspace || workspace_bytes < ffn_workspace(M, F, dtype, gated ? 3 : 1))
+    const size_t need = ffn_workspace(M, F, dtype, gated ? 3 : 1);
+    if (!workspace || workspace_bytes < need)
         return NG_ERR_WORKSPACE;
-    range_t rw = rng(workspace, M * F * (gated ? 3 : 1));
+    /* bytes the library may touch: the required size, or h (rounded to 256
+     * bytes) followed by two fp32 partial sums of y when the caller's
+     * workspace is that large (split K of the second GEMM) */
+    size_t touch = need;
+    if ((size_t)M * (size_t)N <= (SIZE_MAX / 16u) - ((size_t)M * (size_t)F)) {
+        const size_t split = ffn_workspace(M, F, dtype, 1) + 8u * (size_t)M * (size_t)N;
+        if (split > touch)
+            touch = split <= workspace_bytes ? split : need;
+    }
+    range_t rw;
+    rw.lo = (uintptr_t)workspace;
+    rw.hi = rw.lo + touch;
     if (overlap(rw, ry))
         return NG_ERR_ALIAS;
     for (int i = 0; i < 7; ++i)

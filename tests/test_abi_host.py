@@ -105,6 +105,16 @@ def test_fused_ffn_validation_errors(kw, status):
     assert ffn(**kw) == status
 
 
+# A workspace large enough for the split-K partials of y (h, 256 bytes here,
+# then 8 M N bytes) is alias-checked over all of them; a smaller one only
+# over h.
+@no_gpu_only
+def test_fused_ffn_split_k_workspace_is_alias_checked():
+    assert ffn(wsb=256 + 8 * 4 * 8, y=WS + 300) == ALIAS
+    assert ffn(wsb=256 + 8 * 4 * 8, x=WS + 400) == ALIAS
+    assert gffn(wsb=3 * 4 * 32 * 2, y=WS + 700) == ALIAS
+
+
 def gffn(x=X, g=G, b=B, w1=W, b1=BI, w2=0x90000000, b2=0xA0000000, y=Y, M=4, K=16, F=32, N=8,
          eps=1e-5, norm=1, act=1, dtype=0, ws=WS, wsb=3 * 4 * 32 * 2):
     return ng.lib.fused_gated_ffn(x, g, b, w1, b1, w2, b2, y, M, K, F, N, eps, norm, act, dtype,

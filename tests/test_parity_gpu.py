@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import synth
-from helpers import TOL, assert_close, run_case_gpu, sample_indices, to_f64, upload
+from helpers import TOL, assert_close, run_case_gpu, sample_indices, tdtype, to_f64, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -392,6 +392,31 @@ def test_stacked_qkv_weight_equals_three_calls(M):
         assert torch.equal(y.view(torch.int16), joined.view(torch.int16))
     else:
         assert_close(to_f64(joined), to_f64(y), tol=2e-3, what="qkv parts")
+
+
+@pytest.mark.parametrize("M,K,F,N,dtype", [(100, 264, 520, 136, F16), (300, 512, 2000, 512, BF16),
+                                            (64, 136, 200, 72, F16)])
+def test_ffn_split_k_of_the_second_gemm(M, K, F, N, dtype):
+    """A workspace with room for two fp32 partial sums of y splits the second
+    GEMM's K over two workgroups per tile (its tiles fill under half of the
+    CUs; F = 200 leaves a ragged last step in the second range): parity
+    with the oracle, run-to-run identical, and close to the unsplit call."""
+    import norm_gemm_amd as ng
+    case = synth.make_ffn(f"ffn_splitk_{M}x{K}x{F}x{N}", M, K, F, N, dtype=dtype, norm=LN,
+                          act=SILU, gamma=True, beta=True, b1=True, b2=True, seed=M + F)
+    A = case.arrays
+    u = lambda k: upload(A[k], dtype)
+    args = (u("x"), u("W1"), u("W2"), u("gamma"), u("beta"), u("b1"), u("b2"))
+    need = ng.fused_ffn_workspace_size(M, F, tdtype(dtype))
+    big = torch.empty(need + 8 * M * N + 4096, dtype=torch.uint8, device="cuda")
+    y1 = ng.fused_ffn(*args, eps=1e-5, norm=LN, act="silu", workspace=big)
+    y2 = ng.fused_ffn(*args, eps=1e-5, norm=LN, act="silu", workspace=big)
+    y0 = ng.fused_ffn(*args, eps=1e-5, norm=LN, act="silu")
+    torch.cuda.synchronize()
+    ref = oracle.run_case(case)
+    assert_close(to_f64(y1), ref, what=case.name)
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    assert_close(to_f64(y1), to_f64(y0), tol=5e-3, what="split vs unsplit")
 
 
 @pytest.mark.parametrize("M", [16, 100])
