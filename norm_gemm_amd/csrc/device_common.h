@@ -218,6 +218,16 @@ __device__ __forceinline__ void dma16(const void *sbase, uint32_t voff, uint32_t
                  : "memory", "m0");
 }
 
+// The same direct load with a per-lane 64-bit address (lanes may read from
+// different arrays); inactive lanes neither read nor write LDS.
+__device__ __forceinline__ void dma16_ptr(const void *p, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(p), "s"(lds)
+                 : "memory", "m0");
+}
+
 // ------------------------------------------------ explicit register load
 // One 16-byte-per-lane load into registers (global_load_dwordx4, scalar base
 // + 32-bit vector offset) issued as inline asm: the compiler's own vmcnt

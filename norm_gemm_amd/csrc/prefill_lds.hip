@@ -11,18 +11,26 @@
 //               the tile's own rows of y, which the main kernel reads before
 //               it writes them (an in-kernel prologue is used when y cannot
 //               serve as scratch).
-//   K loop      BK = 64, three LDS stages, loads two steps ahead. x, gamma,
-//               beta and W go HBM -> LDS by direct 128-bit loads (no
-//               registers), issued one after each pair of MFMAs so that the
-//               load unit stays busy while the matrix cores run. Halfway
-//               through step k each lane normalizes the x chunks of step k + 1
-//               that its own loads brought in (fp16: packed fp16 arithmetic;
-//               bf16: fp32), in place, so the normalized x lives only in LDS.
+//   K loop      BK = 64, three LDS stages, W loads two steps ahead. W goes
+//               HBM -> LDS by direct 128-bit loads (no registers), one after
+//               each pair of MFMAs so that the load unit stays busy while the
+//               matrix cores run; so does x when it is not normalized. With
+//               normalization each lane loads its x chunks of step k + 1
+//               into registers at the start of step k, normalizes them in its
+//               last sub-step (fp16: packed fp16 arithmetic; bf16: fp32) and
+//               writes them once into the next stage, so the normalized x
+//               lives only in registers and LDS. gamma and beta come with x,
+//               or, when both are given, through small LDS slots loaded by
+//               one wave per workgroup two steps ahead.
+//   gated       (GT) a tile's 256 W rows are the gate and up rows of 128
+//               output columns; the epilogue forms act(gate) * up.
+//   split K     (SK) workgroups split the K steps of a tile in two and write
+//               fp32 partials, summed in order by a second kernel.
 //   MFMA        v_mfma_f32_32x32x16 with W as the first operand and normalized
 //               x as the second, so each 32x32 result block is y^T: lane l
 //               holds output row m = l % 32 and four consecutive columns.
 //               Fragments of the next sub-step are read ahead.
-//   epilogue    + bias, optional SiLU, one rounding, staged through LDS into
+//   epilogue    + bias, optional activation, one rounding, staged through LDS into
 //               row-major order and written with 128-bit stores.
 //
 // Workgroups are dealt to the 8 XCDs round-robin. When the shape allows, the
@@ -195,6 +203,9 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
     // One LDS object per pipeline stage and operand
     __shared__ u32x4 A0[A_TILE], A1[A_TILE], A2[A_TILE];
     __shared__ u32x4 B0[B_TILE], B1[B_TILE], B2[B_TILE];
+    // gamma (chunks 0-7) and beta (chunks 8-15) of one K step, in three slots
+    // used like the stages (see the K step); one chunk per lane of a wave
+    __shared__ u32x4 G0[64], G1[64], G2[64];
     auto Ast = [&](auto sc) -> u32x4 * {
         constexpr int i = decltype(sc)::value % NSTAGE;
         if constexpr (i == 0)
@@ -212,6 +223,15 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
             return B1;
         else
             return B2;
+    };
+    auto Gst = [&](auto sc) -> u32x4 * {
+        constexpr int i = decltype(sc)::value % NSTAGE;
+        if constexpr (i == 0)
+            return G0;
+        else if constexpr (i == 1)
+            return G1;
+        else
+            return G2;
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
@@ -408,20 +428,52 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
     // x / gamma / beta chunks of K step kt into registers (asynchronous: see
     // ldg16_async; NXL loads, completed by wait_vmcnt_tied)
     constexpr int NXL = A_DMA + (HG ? 1 : 0) + (HB ? 1 : 0);
-    auto load_raw = [&](int kt, NormRaw &r) {
+    // With both gamma and beta they come through LDS slots (issue_gb); with
+    // one of them, straight into registers with x (measured faster there).
+    constexpr bool RING = HG && HB;
+    auto load_gb_regs = [&](int kt, NormRaw &r) {
         kt = min(kt, nk - 1);
         const bool tl = KT && kt == nk - 1;
-        const char *xb = reinterpret_cast<const char *>(xtile) + (size_t)kt * (BK * 2);
         const char *gb = reinterpret_cast<const char *>(gamma) + (size_t)kt * (BK * 2);
         const char *bb = reinterpret_cast<const char *>(beta) + (size_t)kt * (BK * 2);
-#pragma unroll
-        for (int i = 0; i < A_DMA; ++i)
-            r.v[i] = ldg16_async(xb, tl ? aoff_t[i] : aoff_g[i]);
-        r.g = r.b = u32x4{0u, 0u, 0u, 0u};
         if constexpr (HG)
             r.g = ldg16_async(gb, tl ? goff_t : goff);
         if constexpr (HB)
             r.b = ldg16_async(bb, tl ? goff_t : goff);
+    };
+    auto load_raw = [&](int kt, NormRaw &r) {
+        kt = min(kt, nk - 1);
+        const bool tl = KT && kt == nk - 1;
+        const char *xb = reinterpret_cast<const char *>(xtile) + (size_t)kt * (BK * 2);
+#pragma unroll
+        for (int i = 0; i < A_DMA; ++i)
+            r.v[i] = ldg16_async(xb, tl ? aoff_t[i] : aoff_g[i]);
+        r.g = r.b = u32x4{0u, 0u, 0u, 0u};
+        if constexpr (!RING)
+            load_gb_regs(kt, r);
+    };
+    // gamma / beta of K step kt into a slot: one direct load by wave 0 alone,
+    // lanes 0-7 the gamma chunks and 8-15 the beta chunks (past K: the last
+    // valid chunk; the other lanes repeat them). All waves of all CUs loading
+    // the same two lines every step would queue their requests at one L2
+    // channel; this is one request per line per CU and step. Issued two steps
+    // ahead: wave 0's waits on its x loads of the same step cover it, and the
+    // step's barrier publishes it.
+    auto issue_gb = [&](int kt, u32x4 *Gs) {
+        if constexpr (RING) {
+            if (wave == 0) {
+                kt = min(kt, nk - 1);
+                const int c = lane & 7;
+                const int k = (kt * BK + c * 8 < K) ? kt * BK + c * 8 : kl + clast * 8;
+                dma16_ptr(((lane & 8) == 0 ? gamma : beta) + k, lds_addr(Gs));
+            }
+        }
+    };
+    auto read_gb = [&](const u32x4 *Gs, NormRaw &r) {
+        if constexpr (RING) {
+            r.g = Gs[ach[0]];
+            r.b = Gs[CPR + ach[0]];
+        }
     };
     auto nrm_store = [&](int kt, u32x4 *As, const NormRaw &r) {
         const bool kin = kt * BK + ach[0] * 8 < K;
@@ -500,6 +552,9 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
     if constexpr (AFFINE) {
         NormRaw r0;
         load_raw(0, r0);
+        if constexpr (RING)
+            load_gb_regs(0, r0);
+        issue_gb(1, G1);
         issue(0, A0, B0);
         issue(1, A1, B1);
         wait_vmcnt_tied<2 * LPS>(r0.v[0], r0.v[1], r0.g, r0.b);
@@ -600,6 +655,7 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
         issue_fence(x, gamma, beta);
         if constexpr (AFFINE) {
             static_assert(LPS == 4, "one W load per sub-step");
+            issue_gb(kt + 2, Gst(S2{}));
             NormRaw raw;
             load_raw(kt + 1, raw);
             sb();
@@ -627,6 +683,7 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
             mm(f0, 1);
             sb();
             wait_vmcnt_tied<3>(raw.v[0], raw.v[1], raw.g, raw.b);
+            read_gb(Gst(S1{}), raw);
             mm(f1, 0);
             // (in the last step this normalizes a stage that is never read)
             nrm_store(kt + 1, Ast(S1{}), raw);
