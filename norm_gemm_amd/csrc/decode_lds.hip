@@ -118,6 +118,13 @@ __global__ __launch_bounds__(64 * kNW) void decode_lds_kernel(
     const int kbpw = (nkb + kNW - 1) / kNW;
     const int kb0 = min(wave * kbpw, nkb);
     const int kb1 = min(kb0 + kbpw, nkb);
+    // Each workgroup walks its waves' ranges from a different starting
+    // k-block (logical k-block kb is physical block kp(kb)): every CU reads
+    // all of x and gamma, and in lockstep all CUs would request the same
+    // lines of them at once, queueing at one L2 channel per line.
+    const int nrange = max(kb1 - kb0, 1);
+    const int rot = (int)blockIdx.x % nrange;
+    auto kp = [&](int kb) { return kb0 + (kb - kb0 + rot) % nrange; };
 
     // Direct loads of block (kb, NB) into slot NB: load h (0/1) puts row
     // 8h + lane/8 at chunk position lane%8, holding logical chunk
@@ -132,6 +139,7 @@ __global__ __launch_bounds__(64 * kNW) void decode_lds_kernel(
             kb = kb1 - 1;
             nb = NBK - 1;
         }
+        kb = kp(kb);
         u32x4 *dst = slot(NB, wave);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -152,7 +160,7 @@ __global__ __launch_bounds__(64 * kNW) void decode_lds_kernel(
     const uint16_t *bp = beta ? beta : x;
     auto load_x = [&](auto SET, int kb) {
         constexpr int set = decltype(SET)::value;
-        kb = min(kb, nkb - 1);
+        kb = kp(min(kb, kb1 - 1));
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
             const int k = kb * 64 + (4 * s2 + lg) * 8;
@@ -293,7 +301,8 @@ __global__ __launch_bounds__(64 * kNW) void decode_lds_kernel(
             wait_vmcnt<2 * D>();
         }
         u32x4 xf[MB][2];
-        x_frags(SET, kb, xf);
+        const int kbp = kp(kb);           // physical k-block
+        x_frags(SET, kbp, xf);
         static_for<0, NBK>([&](auto NB) {
             constexpr int nb = decltype(NB)::value;
             constexpr int nb_next = (nb + D) % NBK;
@@ -306,12 +315,12 @@ __global__ __launch_bounds__(64 * kNW) void decode_lds_kernel(
             else
                 wait_vmcnt<2 * D>();
             u32x4 *sl = slot(NB, wave);
-            if (kb * 64 + 64 > K) {
+            if (kbp * 64 + 64 > K) {
                 // zero the chunks past K of this lane's own direct loads
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const int row = 8 * h + drow0;
-                    if (kb * 64 + dswz(row, lane & 7) * 8 >= K)
+                    if (kbp * 64 + dswz(row, lane & 7) * 8 >= K)
                         sl[h * 64 + lane] = u32x4{0u, 0u, 0u, 0u};
                 }
             }

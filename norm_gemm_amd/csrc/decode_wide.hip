@@ -113,6 +113,13 @@ __global__ __launch_bounds__(64 * kNW) void decode_wide_kernel(
     const int kbpw = (nkb + kNW - 1) / kNW;
     const int kb0 = min(wave * kbpw, nkb);
     const int kb1 = min(kb0 + kbpw, nkb);
+    // Each workgroup walks its waves' ranges from a different starting
+    // k-block (logical k-block kb is physical block kp(kb)): every CU reads
+    // all of x and gamma, and in lockstep all CUs would request the same
+    // lines of them at once, queueing at one L2 channel per line.
+    const int nrange = max(kb1 - kb0, 1);
+    const int rot = (int)blockIdx.x % nrange;
+    auto kp = [&](int kb) { return kb0 + (kb - kb0 + rot) % nrange; };
     const bool has_work = kb0 < kb1;
 
     // Direct loads of block (kb, nb) into slot SL: load q (0..7) puts row
@@ -136,6 +143,8 @@ __global__ __launch_bounds__(64 * kNW) void decode_wide_kernel(
             nb = NBK - 1;
         }
         kb = max(kb, 0);
+        if (kb >= kb0 && kb < kb1)
+            kb = kp(kb);
         u32x4 *dst = slot(SL, wave);
         const uint16_t *wb = W + (int64_t)(n0 + nb * 16) * K;
 #pragma unroll
@@ -155,6 +164,8 @@ __global__ __launch_bounds__(64 * kNW) void decode_wide_kernel(
     const uint16_t *xrow = x + (int64_t)min(lr, M - 1) * K;
     auto load_x = [&](int kb) {
         kb = min(kb, nkb - 1);
+        if (kb >= kb0 && kb < kb1)
+            kb = kp(kb);
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
             const int k = kb * kKB + (4 * s + lg) * 8;
@@ -330,7 +341,8 @@ __global__ __launch_bounds__(64 * kNW) void decode_wide_kernel(
         constexpr bool next = decltype(NEXT)::value;
         wait_vmcnt<BL * (NBK >= 2 ? 2 : 1)>();
         u32x4 xf[8];
-        x_frags(kb, xf);
+        const int kbp = kp(kb);           // physical k-block
+        x_frags(kbp, xf);
         // the raw registers are free only after x_frags: keep the next
         // k-block's loads behind it (else both register sets are live)
         issue_fence(x, gamma, beta);
@@ -345,11 +357,11 @@ __global__ __launch_bounds__(64 * kNW) void decode_wide_kernel(
             else
                 wait_vmcnt<BL>();
             u32x4 *blk = slot(ic<sl>{}, wave);
-            if (kb * kKB + kKB > K) {
+            if (kbp * kKB + kKB > K) {
                 // zero the chunks past K of this lane's own direct loads
 #pragma unroll
                 for (int q = 0; q < 8; ++q) {
-                    if (kb * kKB + (lchunk ^ (2 * q)) * 8 >= K)
+                    if (kbp * kKB + (lchunk ^ (2 * q)) * 8 >= K)
                         blk[q * 64 + lane] = u32x4{0u, 0u, 0u, 0u};
                 }
             }
