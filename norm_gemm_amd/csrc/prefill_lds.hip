@@ -428,8 +428,9 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
     // x / gamma / beta chunks of K step kt into registers (asynchronous: see
     // ldg16_async; NXL loads, completed by wait_vmcnt_tied)
     constexpr int NXL = A_DMA + (HG ? 1 : 0) + (HB ? 1 : 0);
-    // With both gamma and beta they come through LDS slots (issue_gb); with
-    // one of them, straight into registers with x (measured faster there).
+    // With both gamma and beta they come through LDS slots (issue_gb), read
+    // at the start of the step before the one that uses them; with one of
+    // them, straight into registers with x (measured faster there).
     constexpr bool RING = HG && HB;
     auto load_gb_regs = [&](int kt, NormRaw &r) {
         kt = min(kt, nk - 1);
@@ -469,6 +470,8 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
             }
         }
     };
+    // (only with RING: otherwise the slots are never written and gamma / beta
+    // came into registers with x)
     auto read_gb = [&](const u32x4 *Gs, NormRaw &r) {
         if constexpr (RING) {
             r.g = Gs[ach[0]];
@@ -658,6 +661,8 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
             issue_gb(kt + 2, Gst(S2{}));
             NormRaw raw;
             load_raw(kt + 1, raw);
+            // published by the barrier that ended step kt - 1
+            read_gb(Gst(S1{}), raw);
             sb();
             rdfrag(Ac, Bc, 0, f0);
             sb();
@@ -683,7 +688,6 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
             mm(f0, 1);
             sb();
             wait_vmcnt_tied<3>(raw.v[0], raw.v[1], raw.g, raw.b);
-            read_gb(Gst(S1{}), raw);
             mm(f1, 0);
             // (in the last step this normalizes a stage that is never read)
             nrm_store(kt + 1, Ast(S1{}), raw);
