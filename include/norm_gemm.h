@@ -102,7 +102,9 @@ int fused_norm_gemm(const void *x, const void *gamma, const void *beta,
  * is then split over two workgroups per tile and the partials are added in a
  * fixed order (deterministic) by a second kernel. Every workspace byte the
  * call may touch is checked against the inputs and y (NG_ERR_ALIAS).
- * Two kernel launches on `stream`, in order. The workspace must not overlap
+ * All kernels (the statistics pass when normalizing with M > 32, the two
+ * GEMMs, the partial sum when K is split) run on `stream`, in order, without
+ * synchronizing. The workspace must not overlap
  * any input or y; it may be reused once the call's work has completed on the
  * stream. Returns an ng_status_t.
  */
