@@ -29,14 +29,21 @@
  *    beta, W, bias and y. x is [M,K], W is [N,K] (K contiguous, the "w.T"
  *    convention of the pages), gamma/beta are [K], bias is [N], y is [M,N].
  *  - Pointers must be at least 2-byte aligned; 16-byte aligned pointers with
- *    K % 8 == 0 take 128-bit loads, anything else uses element loads in the
- *    same kernels. Any M, N, K >= 1 is supported.
+ *    K % 8 == 0 take 128-bit loads, anything else uses element loads. Any
+ *    M, N, K (and F) in [1, 2^31 - 1] is supported. The tiled MFMA kernel
+ *    addresses the rows of a tile with 32-bit byte offsets, so it serves
+ *    aligned calls with M > 32 only up to K = 8,388,600 (256 rows of K
+ *    elements below 2^32 bytes); larger K takes the generic tiled kernel,
+ *    which forms 64-bit row addresses. The same bound, on F + 256 rows,
+ *    selects the gated FFN's one-kernel phase 1.
  *  - gamma == NULL means gamma = 1; beta == NULL means beta = 0; bias == NULL
  *    means no bias. With norm == NG_NORM_NONE, gamma, beta and eps are ignored.
  *  - y is overwritten, never accumulated into. y must not overlap any input.
  *  - stream is a hipStream_t (NULL = the null stream). Work is enqueued on it
- *    and the call returns without synchronizing. Nothing is allocated, no
- *    global state is kept; calls are re-entrant and thread-safe.
+ *    and the call returns without synchronizing. Nothing is allocated. The
+ *    only process-wide state is a cache of each device's compute-unit count,
+ *    filled on a device's first call and read-only after; calls are
+ *    re-entrant and thread-safe.
  *  - On any validation error no kernel is launched and y is untouched. A
  *    launch failure reports NG_ERR_HIP. Faults inside a kernel surface, as in
  *    HIP, at the caller's next synchronization.

@@ -32,7 +32,7 @@ C_FLAGS = ["-O2", "-std=c11", "-fPIC", "-Wall", "-Wextra", f"-I{INCLUDE}", f"-I{
 
 SOURCES = ["api.cpp", "prefill.hip", "prefill_lds.hip", "decode.hip", "decode_lds.hip", "decode_wide.hip",
            "gated.hip"]
-C_SOURCES = ["validate.c"]
+C_SOURCES = ["validate.c", "route.c"]
 
 
 def _compile(src: str) -> str:

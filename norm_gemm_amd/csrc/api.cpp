@@ -2,9 +2,34 @@
 // validate (pure host code), pick the kernel, launch on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "launch.h"
 #include "norm_gemm.h"
+#include "route.h"
 #include "validate.h"
+
+namespace ng {
+
+int cu_count()
+{
+    // one entry per device ordinal; filled on first use, read-only after
+    constexpr int kMaxDev = 64;
+    static std::atomic<int> cache[kMaxDev];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return 256;
+    int c = (dev >= 0 && dev < kMaxDev) ? cache[dev].load(std::memory_order_relaxed) : 0;
+    if (c > 0)
+        return c;
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c < 1)
+        c = 256;
+    if (dev >= 0 && dev < kMaxDev)
+        cache[dev].store(c, std::memory_order_relaxed);
+    return c;
+}
+
+}  // namespace ng
 
 namespace {
 
@@ -33,14 +58,13 @@ ng::GemmArgs make_args(const void *x, const void *gamma, const void *beta, const
 int run(const ng::GemmArgs &a, hipStream_t s)
 {
     hipError_t e;
-    if (a.M <= ng::kDecodeMaxM)
-        e = !a.vec ? ng::launch_decode(a, s)
-                   : (ng::decode_wide_fits(a) ? ng::launch_decode_wide(a, s)
-                                              : ng::launch_decode_lds(a, s));
-    else if (a.vec)
-        e = ng::launch_prefill_lds(a, s);
-    else
-        e = ng::launch_prefill(a, s);
+    switch (ng_route_gemm(a.M, a.N, a.K, a.vec ? 1 : 0, ng::cu_count())) {
+    case NG_ROUTE_DECODE_ELEM: e = ng::launch_decode(a, s); break;
+    case NG_ROUTE_DECODE_WIDE: e = ng::launch_decode_wide(a, s); break;
+    case NG_ROUTE_DECODE_LDS: e = ng::launch_decode_lds(a, s); break;
+    case NG_ROUTE_PREFILL_LDS: e = ng::launch_prefill_lds(a, s); break;
+    default: e = ng::launch_prefill(a, s); break;
+    }
     return e == hipSuccess ? NG_OK : NG_ERR_HIP;
 }
 
@@ -53,13 +77,12 @@ int ffn_down(const void *h, const void *W2, const void *b2, void *y, int64_t M, 
 {
     const ng::GemmArgs a = make_args(h, nullptr, nullptr, W2, b2, y, M, N, F, 0.0f,
                                      NG_NORM_NONE, NG_ACT_NONE, dtype);
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) == hipSuccess)
-        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const int cus = ng::cu_count();
     const size_t hbytes = (((size_t)M * (size_t)F * 2u) + 255u) & ~(size_t)255u;
     const size_t pbytes = 2u * (size_t)M * (size_t)N * 4u;
     char *part = (char *)workspace + hbytes;
-    if (a.vec && M > ng::kDecodeMaxM && cus > 0 && 2 * ng::prefill_tiles(M, N) <= cus &&
+    if (ng_route_gemm(M, N, F, a.vec ? 1 : 0, cus) == NG_ROUTE_PREFILL_LDS &&
+        2 * ng::prefill_tiles(M, N) <= cus &&
         ng::prefill_k_steps(F) >= 4 && workspace_bytes >= hbytes + pbytes &&
         ((uintptr_t)part & 15u) == 0) {
         if (ng::launch_prefill_lds_splitk(a, (float *)part, 2, s) != hipSuccess ||
@@ -127,7 +150,7 @@ int fused_gated_ffn(const void *x, const void *gamma, const void *beta, const vo
     char *h = (char *)workspace;
     // phase 1: h = act(a . W_gate^T + b_gate) * (a . W_up^T + b_up)
     const ng::GemmArgs a = make_args(x, gamma, beta, W1, b1, h, M, F, K, eps, norm, act, dtype);
-    if (ng::prefill_gated_fits(a)) {
+    if (ng_gated_tiled_fits(M, F, K, a.vec ? 1 : 0)) {
         if (ng::launch_prefill_lds_gated(a, s) != hipSuccess)
             return NG_ERR_HIP;
     } else {

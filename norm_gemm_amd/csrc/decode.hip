@@ -206,10 +206,8 @@ hipError_t launch_t(const GemmArgs &a, int nbk, int grid, hipStream_t s)
 template <int DT>
 hipError_t launch_dt(const GemmArgs &a, int nbk, int grid, hipStream_t s)
 {
+    // element loads only: aligned skinny calls take the line or wide kernels
     const bool affine = a.norm != NORM_NONE;
-    if (a.vec)
-        return affine ? launch_t<DT, true, true>(a, nbk, grid, s)
-                      : launch_t<DT, false, true>(a, nbk, grid, s);
     return affine ? launch_t<DT, true, false>(a, nbk, grid, s)
                   : launch_t<DT, false, false>(a, nbk, grid, s);
 }
@@ -218,11 +216,7 @@ hipError_t launch_dt(const GemmArgs &a, int nbk, int grid, hipStream_t s)
 
 hipError_t launch_decode(const GemmArgs &a, hipStream_t s)
 {
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess)
-        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (cus < 1)
-        cus = 256;
+    const int cus = cu_count();
     // enough 16-row blocks per workgroup for about one workgroup per CU
     const int64_t blocks = (a.N + 15) / 16;
     int nbk = (int)((blocks + cus - 1) / cus);

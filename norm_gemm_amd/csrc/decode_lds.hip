@@ -431,11 +431,7 @@ hipError_t launch_nbk(const GemmArgs &a, int nbk, int grid, hipStream_t s)
 
 hipError_t launch_decode_lds(const GemmArgs &a, hipStream_t s)
 {
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess)
-        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (cus < 1)
-        cus = 256;
+    const int cus = cu_count();
     // about one workgroup per CU: the fewest row blocks per workgroup that
     // cover N in one pass over the CUs, at least 2 (one in flight), at most 8
     const int64_t blocks = (a.N + 15) / 16;

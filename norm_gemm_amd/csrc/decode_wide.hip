@@ -32,6 +32,7 @@
 
 #include "device_common.h"
 #include "launch.h"
+#include "route.h"
 
 namespace ng {
 namespace {
@@ -485,34 +486,11 @@ hipError_t launch_dt(const GemmArgs &a, int nbk, int grid, hipStream_t s)
 
 }  // namespace
 
-int decode_wide_row_blocks(int64_t N)
-{
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess)
-        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (cus < 1)
-        cus = 256;
-    // about one workgroup per CU: the fewest row blocks per workgroup that
-    // cover N in one pass over the CUs, at most 8; 0 when N < 16 rows
-    const int64_t blocks = (N + 15) / 16;
-    int64_t nbk = (blocks + cus - 1) / cus;
-    nbk = nbk < 1 ? 1 : (nbk > kNBMax ? kNBMax : nbk);
-    while (nbk > 1 && N < 16 * nbk)
-        --nbk;
-    return N >= 16 * nbk ? (int)nbk : 0;
-}
-
-bool decode_wide_fits(const GemmArgs &a)
-{
-    const int nbk = decode_wide_row_blocks(a.N);
-    return a.M <= 16 && nbk > 0 && (int64_t)nbk * 16 * a.K * 2 <= INT32_MAX;
-}
-
 hipError_t launch_decode_wide(const GemmArgs &a, hipStream_t s)
 {
-    const int nbk = decode_wide_row_blocks(a.N);
+    const int nbk = ng_decode_wide_row_blocks(a.N, cu_count());
     // byte offsets within a slab are 32-bit
-    if (a.M > 16 || nbk == 0 || (int64_t)nbk * 16 * a.K * 2 > INT32_MAX)
+    if (ng_route_gemm(a.M, a.N, a.K, a.vec ? 1 : 0, cu_count()) != NG_ROUTE_DECODE_WIDE)
         return hipErrorInvalidValue;
     const int64_t blocks = (a.N + 15) / 16;
     const int grid = (int)((blocks + nbk - 1) / nbk);

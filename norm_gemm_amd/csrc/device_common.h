@@ -291,49 +291,40 @@ __device__ __forceinline__ void lds_barrier()
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef short short2_t __attribute__((ext_vector_type(2)));
 
-// Partial sums of one 8-element chunk for the row statistics, accumulated in
-// fp32 with the packed dot products of gfx950 (v_dot2_f32_f16 / _bf16):
+// Partial sums of one 8-element chunk for the row statistics, in fp32:
 //   LayerNorm: d = x - shift (shift = the row's first element), s1 += sum d,
 //              s2 += sum d^2;  RMSNorm: s2 += sum x^2.
-// fp16: the shift is a packed fp16 subtraction (exact whenever x and the
-// shift are within a factor of two of each other; otherwise rounded once to
-// 11 bits, which perturbs the variance only at that relative level).
-// bf16: shifted sums in fp32 for LayerNorm, packed bf16 dots for RMSNorm.
+// LayerNorm: the shifted difference x - shift is formed in fp32 (exact for
+// both formats, and no overflow for fp16 rows spanning more than its range);
+// RMSNorm: the packed dot products of gfx950 (v_dot2_f32_f16 / _bf16) of x
+// with itself (the products are exact in fp32).
 template <int DT, bool LN>
 __device__ __forceinline__ void stats_chunk(const u32x4 &c, uint32_t shift2, float &s1, float &s2)
 {
-    if constexpr (DT == DT_F16) {
-        const half2_t one = {(_Float16)1.0f, (_Float16)1.0f};
+    if constexpr (LN) {
+        const float sh = lo_to_f<DT>(shift2);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             // copy the element first: hipcc mis-lowers __builtin_bit_cast of an
             // element of a vector reference (it re-reads element 0)
             const uint32_t w = c[i];
+            const float d0 = lo_to_f<DT>(w) - sh, d1 = hi_to_f<DT>(w) - sh;
+            s1 += d0 + d1;
+            s2 = fmaf(d0, d0, fmaf(d1, d1, s2));
+        }
+    } else if constexpr (DT == DT_F16) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t w = c[i];
             half2_t x = __builtin_bit_cast(half2_t, w);
-            if constexpr (LN) {
-                half2_t d = x - __builtin_bit_cast(half2_t, shift2);
-                s1 = __builtin_amdgcn_fdot2(d, one, s1, false);
-                s2 = __builtin_amdgcn_fdot2(d, d, s2, false);
-            } else {
-                s2 = __builtin_amdgcn_fdot2(x, x, s2, false);
-            }
+            s2 = __builtin_amdgcn_fdot2(x, x, s2, false);
         }
     } else {
-        if constexpr (LN) {
-            const float sh = lo_to_f<DT_BF16>(shift2);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float d0 = lo_to_f<DT_BF16>(c[i]) - sh, d1 = hi_to_f<DT_BF16>(c[i]) - sh;
-                s1 += d0 + d1;
-                s2 = fmaf(d0, d0, fmaf(d1, d1, s2));
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t w = c[i];
-                short2_t x = __builtin_bit_cast(short2_t, w);
-                s2 = __builtin_amdgcn_fdot2_f32_bf16(x, x, s2, false);
-            }
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t w = c[i];
+            short2_t x = __builtin_bit_cast(short2_t, w);
+            s2 = __builtin_amdgcn_fdot2_f32_bf16(x, x, s2, false);
         }
     }
 }

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "route.h"
+
 namespace ng {
 
 // One validated GEMM request; pointers are device addresses.
@@ -17,13 +19,12 @@ struct GemmArgs {
 };
 
 hipError_t launch_prefill(const GemmArgs &a, hipStream_t s);      // any alignment
-hipError_t launch_prefill_lds(const GemmArgs &a, hipStream_t s);  // a.vec only
+hipError_t launch_prefill_lds(const GemmArgs &a, hipStream_t s);  // route NG_ROUTE_PREFILL_LDS
 hipError_t launch_decode(const GemmArgs &a, hipStream_t s);      // any alignment
 hipError_t launch_decode_lds(const GemmArgs &a, hipStream_t s);  // a.vec only
-hipError_t launch_decode_wide(const GemmArgs &a, hipStream_t s); // a.vec and decode_wide_fits
-bool decode_wide_fits(const GemmArgs &a);  // M <= 16, N >= 16, 32-bit slab offsets
+hipError_t launch_decode_wide(const GemmArgs &a, hipStream_t s); // route NG_ROUTE_DECODE_WIDE
 // gated tiled kernel: a.W = [W_gate; W_up] is [2 a.N, a.K], a.bias [2 a.N]
-bool prefill_gated_fits(const GemmArgs &a);  // a.vec, M > 32, 32-bit W row offsets
+// (only when ng_gated_tiled_fits)
 hipError_t launch_prefill_lds_gated(const GemmArgs &a, hipStream_t s);
 // split K of the plain tiled GEMM (a.vec, no normalization): fp32 partials
 // part[ksplit][M][N], then y = act(sum of the partials + bias)
@@ -36,6 +37,10 @@ hipError_t launch_splitk_sum(const float *part, const void *bias, void *y, int64
 hipError_t launch_gate(const void *gu, void *h, int64_t M, int64_t F, int act, int dtype,
                        hipStream_t s);
 
-constexpr int64_t kDecodeMaxM = 32;
+constexpr int64_t kDecodeMaxM = NG_DECODE_MAX_M;
+
+// Compute units of the current device, queried once per device and cached
+// (256 if the query fails).
+int cu_count();
 
 }  // namespace ng

@@ -17,8 +17,8 @@
 //               matrix cores run; so does x when it is not normalized. With
 //               normalization each lane loads its x chunks of step k + 1
 //               into registers at the start of step k, normalizes them in its
-//               last sub-step (fp16: packed fp16 arithmetic; bf16: fp32) and
-//               writes them once into the next stage, so the normalized x
+//               last sub-step (fp32 arithmetic, one rounding to the operand
+//               type) and writes them once into the next stage, so the normalized x
 //               lives only in registers and LDS. gamma and beta come with x,
 //               or, when both are given, through small LDS slots loaded by
 //               one wave per workgroup two steps ahead.
@@ -41,12 +41,11 @@
 // LDS tiles are [rows][64] 16-bit elements with the 16-byte chunk index XOR-
 // swizzled by (row / 2) % 8; with the MFMA operand pattern (32 rows x one
 // chunk per half-wave) this keeps ds_read_b128 free of bank conflicts.
-#include <stdlib.h>
-
 #include <type_traits>
 
 #include "device_common.h"
 #include "launch.h"
+#include "route.h"
 
 namespace ng {
 namespace {
@@ -86,17 +85,6 @@ __device__ __forceinline__ floatx16 mfma32(const u32x4 &a, const u32x4 &b, const
     else
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-
-// NORM_GEMM_STATS=prologue selects the in-kernel statistics prologue instead of
-// the statistics pass (both are correct; used to compare them by measurement).
-inline bool stats_in_kernel()
-{
-    static const bool v = [] {
-        const char *e = getenv("NORM_GEMM_STATS");
-        return e && e[0] == 'p';
-    }();
-    return v;
 }
 
 struct TileMap {
@@ -395,30 +383,10 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
         __syncthreads();
     }
 
-    // fp16 inputs: the affine step runs in packed fp16 arithmetic (two
-    // elements per instruction, no conversions): ((x - mu_hi) - mu_lo) * rs,
-    // then * gamma + beta; the mean is split into two fp16 parts so that
-    // x - mu stays accurate for rows with a large mean (statistics are fp32)
-    constexpr bool ln = LN;
-    half2_t mu_hi2[A_DMA], mu_lo2[A_DMA], rs2[A_DMA];
-    if constexpr (DT == DT_F16 && AFFINE) {
-#pragma unroll
-        for (int i = 0; i < A_DMA; ++i) {
-            const float mu = ln ? -rnmr[i] / rrs[i] : 0.0f;
-            const _Float16 hi = (_Float16)mu;
-            const _Float16 lo = (_Float16)(mu - (float)hi);
-            mu_hi2[i] = half2_t{hi, hi};
-            mu_lo2[i] = half2_t{lo, lo};
-            // 1/sigma beyond the fp16 range only arises for (near-)constant
-            // rows with a tiny eps, where x - mu is zero: clamp, not inf
-            const _Float16 r = (_Float16)fminf(rrs[i], 65504.0f);
-            rs2[i] = half2_t{r, r};
-        }
-    }
-
-    // x chunks of K step kt that this lane loaded: normalized + affine (fp32
-    // for bf16: x * rs + nmr, then * gamma + beta, one rounding; fp16: see
-    // above), written back in place; rows past M and chunks past K become
+    // x chunks of K step kt that this lane loaded: normalized + affine in
+    // fp32, x * rs + nmr, then * gamma + beta, rounded once to the operand
+    // type (fp16: mixed-precision FMAs read the fp16 inputs directly and the
+    // last one rounds to fp16), written back in place; rows past M and chunks past K become
     // zero. A lane's x rows are A_IST apart: one swizzle, so one logical
     // chunk and one gamma / beta chunk for all of them. Split into the LDS
     // reads and the arithmetic + write so that MFMAs can run in between.
@@ -480,56 +448,30 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
     };
     auto nrm_store = [&](int kt, u32x4 *As, const NormRaw &r) {
         const bool kin = kt * BK + ach[0] * 8 < K;
-        if constexpr (DT == DT_F16) {
+        float g[8], bt[8];
+        if constexpr (HG)
+            unpack8<DT>(r.g, g);
+        if constexpr (HB)
+            unpack8<DT>(r.b, bt);
 #pragma unroll
-            for (int i = 0; i < A_DMA; ++i) {
-                const bool live = alive[i] && kin;
-                u32x4 v = r.v[i];
+        for (int i = 0; i < A_DMA; ++i) {
+            const bool live = alive[i] && kin;
+            float f[8];
+            unpack8<DT>(r.v[i], f);
 #pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    // copy the elements first (bit_cast of a vector element
-                    // reference is miscompiled)
-                    const uint32_t xw = v[d], gd = r.g[d], bd = r.b[d];
-                    half2_t t = __builtin_bit_cast(half2_t, xw);
-                    if constexpr (ln)
-                        t = (t - mu_hi2[i]) - mu_lo2[i];
-                    t = t * rs2[i];
-                    if constexpr (HG && HB)
-                        t = t * __builtin_bit_cast(half2_t, gd) + __builtin_bit_cast(half2_t, bd);
-                    else if constexpr (HG)
-                        t = t * __builtin_bit_cast(half2_t, gd);
-                    else if constexpr (HB)
-                        t = t + __builtin_bit_cast(half2_t, bd);
-                    v[d] = __builtin_bit_cast(uint32_t, t);
-                }
-                As[(i * A_IST + wave * 8) * CPR + lane] = live ? v : u32x4{0u, 0u, 0u, 0u};
+            for (int e = 0; e < 8; ++e) {
+                const float v = fmaf(f[e], rrs[i], rnmr[i]);
+                if constexpr (HG && HB)
+                    f[e] = fmaf(v, g[e], bt[e]);
+                else if constexpr (HG)
+                    f[e] = v * g[e];
+                else if constexpr (HB)
+                    f[e] = v + bt[e];
+                else
+                    f[e] = v;
             }
-        } else {
-            float g[8], bt[8];
-            if constexpr (HG)
-                unpack8<DT>(r.g, g);
-            if constexpr (HB)
-                unpack8<DT>(r.b, bt);
-#pragma unroll
-            for (int i = 0; i < A_DMA; ++i) {
-                const bool live = alive[i] && kin;
-                float f[8];
-                unpack8<DT>(r.v[i], f);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float v = fmaf(f[e], rrs[i], rnmr[i]);
-                    if constexpr (HG && HB)
-                        f[e] = fmaf(v, g[e], bt[e]);
-                    else if constexpr (HG)
-                        f[e] = v * g[e];
-                    else if constexpr (HB)
-                        f[e] = v + bt[e];
-                    else
-                        f[e] = v;
-                }
-                As[(i * A_IST + wave * 8) * CPR + lane] =
-                    live ? pack8<DT>(f) : u32x4{0u, 0u, 0u, 0u};
-            }
+            As[(i * A_IST + wave * 8) * CPR + lane] =
+                live ? pack8<DT>(f) : u32x4{0u, 0u, 0u, 0u};
         }
     };
     // without normalization only the chunks past K of the last step need
@@ -881,11 +823,7 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
 template <int DT, int STATS, int GB, bool KT, bool LN, bool GT, bool SK = false>
 hipError_t launch_k(const GemmArgs &a, hipStream_t s, float *part = nullptr, int ksplit = 1)
 {
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess)
-        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (cus < 1)
-        cus = 256;
+    const int cus = cu_count();
     constexpr int BNO = GT ? BN / 2 : BN;
     TileMap mp;
     mp.tm = (int)((a.M + BM - 1) / BM);
@@ -942,7 +880,7 @@ hipError_t launch_dt(const GemmArgs &a, hipStream_t s)
     // The statistics pass needs 8 bytes of y in every tile's rows: every
     // tile (including the last, partial one) must have at least 4 columns
     // and the rows must be 8-byte aligned.
-    const bool y_scratch = a.N % 8 == 0 && ((uintptr_t)a.y & 15u) == 0 && !stats_in_kernel();
+    const bool y_scratch = a.N % 8 == 0 && ((uintptr_t)a.y & 15u) == 0;
     return y_scratch ? launch_norm<DT, ST_FROM_Y, GT>(a, s) : launch_norm<DT, ST_PROLOGUE, GT>(a, s);
 }
 
@@ -950,14 +888,11 @@ hipError_t launch_dt(const GemmArgs &a, hipStream_t s)
 
 hipError_t launch_prefill_lds(const GemmArgs &a, hipStream_t s)
 {
+    // tile offsets are 32-bit (see ng_tile_offsets_fit)
+    static_assert(BN == NG_TILE_ROWS && BM <= BN, "tile rows");
+    if (ng_route_gemm(a.M, a.N, a.K, a.vec ? 1 : 0, cu_count()) != NG_ROUTE_PREFILL_LDS)
+        return hipErrorInvalidValue;
     return a.dtype == DT_F16 ? launch_dt<DT_F16, false>(a, s) : launch_dt<DT_BF16, false>(a, s);
-}
-
-bool prefill_gated_fits(const GemmArgs &a)
-{
-    // W row offsets within a tile (up to N + 127 rows past its first gate
-    // row) are 32-bit byte offsets
-    return a.vec && a.M > kDecodeMaxM && (a.N + BN) * a.K * 2 <= (int64_t)UINT32_MAX;
 }
 
 int prefill_tiles(int64_t M, int64_t N)
@@ -974,7 +909,8 @@ hipError_t launch_prefill_lds_splitk(const GemmArgs &a, float *part, int ksplit,
                                      hipStream_t s)
 {
     // plain GEMM only; every K range must get at least one step
-    if (!a.vec || a.norm != NORM_NONE || ksplit < 2 || prefill_k_steps(a.K) < 2 * ksplit)
+    if (ng_route_gemm(a.M, a.N, a.K, a.vec ? 1 : 0, cu_count()) != NG_ROUTE_PREFILL_LDS ||
+        a.norm != NORM_NONE || ksplit < 2 || prefill_k_steps(a.K) < 2 * ksplit)
         return hipErrorInvalidValue;
     const bool kt = a.K % BK != 0;
     if (a.dtype == DT_F16)
@@ -986,7 +922,9 @@ hipError_t launch_prefill_lds_splitk(const GemmArgs &a, float *part, int ksplit,
 
 hipError_t launch_prefill_lds_gated(const GemmArgs &a, hipStream_t s)
 {
-    if (!prefill_gated_fits(a))
+    // W row offsets within a tile (up to N + 127 rows past its first gate
+    // row) are 32-bit byte offsets
+    if (!ng_gated_tiled_fits(a.M, a.N, a.K, a.vec ? 1 : 0))
         return hipErrorInvalidValue;
     return a.dtype == DT_F16 ? launch_dt<DT_F16, true>(a, s) : launch_dt<DT_BF16, true>(a, s);
 }

@@ -1,0 +1,48 @@
+/* route.c -- kernel selection (pure host C, no HIP). */
+#include "route.h"
+
+int ng_tile_offsets_fit(int64_t rows, int64_t K)
+{
+    if (rows < 1 || K < 1 || K > ((int64_t)1 << 40))
+        return 0;
+    /* last byte a lane may address: row rows-1, chunk (K/8 rounded up) - 1 */
+    const int64_t last = ((rows - 1) * K + ((K + 7) / 8) * 8) * 2;
+    return last <= (int64_t)0xffffffffLL;
+}
+
+int ng_decode_wide_row_blocks(int64_t N, int cus)
+{
+    if (N < 1)
+        return 0;
+    if (cus < 1)
+        cus = 256;
+    const int64_t blocks = (N + 15) / 16;
+    int64_t nbk = (blocks + cus - 1) / cus;
+    nbk = nbk < 1 ? 1 : (nbk > 8 ? 8 : nbk);
+    while (nbk > 1 && N < 16 * nbk)
+        --nbk;
+    return N >= 16 * nbk ? (int)nbk : 0;
+}
+
+int ng_route_gemm(int64_t M, int64_t N, int64_t K, int vec, int cus)
+{
+    if (M <= NG_DECODE_MAX_M) {
+        if (!vec)
+            return NG_ROUTE_DECODE_ELEM;
+        const int nbk = ng_decode_wide_row_blocks(N, cus);
+        /* the wide kernel addresses a slab of 16 nbk rows with 32-bit offsets;
+         * the line kernel forms 64-bit row addresses */
+        if (M <= 16 && nbk > 0 && ng_tile_offsets_fit(16 * (int64_t)nbk, K) &&
+            (int64_t)nbk * 16 * K * 2 <= 0x7fffffffLL)
+            return NG_ROUTE_DECODE_WIDE;
+        return NG_ROUTE_DECODE_LDS;
+    }
+    if (vec && ng_tile_offsets_fit(NG_TILE_ROWS, K))
+        return NG_ROUTE_PREFILL_LDS;
+    return NG_ROUTE_PREFILL_GENERIC;
+}
+
+int ng_gated_tiled_fits(int64_t M, int64_t F, int64_t K, int vec)
+{
+    return vec && M > NG_DECODE_MAX_M && F >= 1 && ng_tile_offsets_fit(F + NG_TILE_ROWS, K);
+}

@@ -1,0 +1,49 @@
+/* route.h -- which kernel serves a request: pure host logic, no HIP calls,
+ * so that every dispatch decision can be checked without a GPU. */
+#ifndef NG_ROUTE_H
+#define NG_ROUTE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    NG_ROUTE_DECODE_ELEM = 0,   /* element-load skinny kernel: any alignment, M <= 32  */
+    NG_ROUTE_DECODE_WIDE = 1,   /* 512-byte W pieces: aligned, M <= 16                 */
+    NG_ROUTE_DECODE_LDS = 2,    /* 128-byte W lines: aligned, M <= 32                  */
+    NG_ROUTE_PREFILL_LDS = 3,   /* tiled MFMA kernel with 32-bit tile offsets          */
+    NG_ROUTE_PREFILL_GENERIC = 4 /* generic tiled kernel: element loads or 64-bit rows */
+} ng_route_t;
+
+/* Largest M served by the skinny (decode) kernels. */
+#define NG_DECODE_MAX_M 32
+
+/* Rows of W per tile of the tiled MFMA kernel (its largest operand tile). */
+#define NG_TILE_ROWS 256
+
+/* 1 when byte offsets within a tile of `rows` rows of a K-element row-major
+ * operand (row r, 16-byte chunk c < K / 8) stay below 2^32: the tiled
+ * kernels address every tile row from one base with 32-bit offsets. */
+int ng_tile_offsets_fit(int64_t rows, int64_t K);
+
+/* 16-row blocks of W per workgroup of the 512-byte-piece decode kernel on a
+ * device with `cus` compute units (about one workgroup per CU, 1..8), or 0
+ * when N has fewer rows than one such slab. */
+int ng_decode_wide_row_blocks(int64_t N, int cus);
+
+/* Kernel for y[M,N] = act(norm(x)[M,K] . W[N,K]^T + bias); vec = 1 when K % 8
+ * == 0 and x, W, gamma, beta are 16-byte aligned. */
+int ng_route_gemm(int64_t M, int64_t N, int64_t K, int vec, int cus);
+
+/* 1 when the gated tiled kernel can serve W1 = [W_gate; W_up] of 2F rows:
+ * aligned, M above the decode range, and its W row offsets (up to F + 255
+ * rows past a tile's first gate row) within 32 bits. */
+int ng_gated_tiled_fits(int64_t M, int64_t F, int64_t K, int vec);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif
