@@ -57,9 +57,15 @@ def run_case_gpu(case, device="cuda"):
                               eps=case.eps, norm=norm, act=act)
 
 
-def sample_indices(n: int, extra: int, seed: int, tile: int = 128):
-    """Edges of the first, second and last tiles plus random interior indices."""
-    base = {0, 1, n - 1, n - 2, min(n - 1, tile - 1), min(n - 1, tile), n // 2}
+def tile_indices(n: int, tile: int, seed: int, interior: int = 1):
+    """Both edges of every `tile`-sized block of range(n) plus `interior`
+    seeded indices inside each block: every tile of the output is compared,
+    with its first and last row (or column) among them."""
     rng = np.random.default_rng(seed)
-    base |= set(int(v) for v in rng.integers(0, n, size=extra))
-    return sorted(i for i in base if 0 <= i < n)
+    out = set()
+    for b0 in range(0, n, tile):
+        b1 = min(n, b0 + tile) - 1
+        out.update((b0, b1))
+        if b1 > b0 + 1 and interior:
+            out.update(int(v) for v in rng.integers(b0 + 1, b1, size=interior))
+    return sorted(out)
