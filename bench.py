@@ -3,19 +3,28 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-Defaults: K = 100 timed steps after W = 400 untimed ones (the clock reaches
-its steady state under load only after tens of milliseconds).
-
 A step is one call of the hot path on one batch of synthetic input that is
-already resident in device memory. The default workload is LayerNorm +
-Linear + bias on x[1024, 8192] (batch 8 x seq 128) and W[8192, 8192] in fp16.
-W is rotated over several device copies so that timed calls stream it from
-HBM instead of the 256 MB last-level cache.
+already resident in device memory. The headline workload is RMSNorm + MatMul
++ SiLU on x[512, 14336] and W[49152, 14336] in fp16 (the fused norm + GEMM +
+SiLU configuration the metric is quoted on). W is rotated over device copies
+so that timed calls stream it from HBM instead of the 256 MB last-level cache.
 
-Prints ONE JSON line with the throughput, a roofline object for the kernel
-(algorithmic FLOPs or bytes per launch over the average launch duration,
-measured with HIP events on the launch stream) and the fp64 CPU oracle timed
-on a bounded sample of the same workload.
+The same process also measures the other workloads of the path, before the
+headline one, and reports them under "workloads" in the same JSON line:
+LayerNorm + Linear + bias (x[64,256] latency and x[1024,8192]), the fused
+FFN (x[512,14336], 49152 -> 14336) and the decode GEMM x[M,8192] .
+W[28672,8192] in bf16 for M = 1, 8, 32. Each is timed the same way, with
+max(W, 100) warmup and max(K, 20) timed steps.
+
+Timing: K steps back to back between two HIP events recorded on the stream
+the kernels are launched on; `value` and `roofline.achieved` are algorithmic
+FLOPs (or bytes) per step over that time per step. One step of a normalizing
+call with M > 32 is two launches (row statistics, then the main kernel),
+which the per-step time includes.
+
+Prints ONE JSON line with the throughput, the roofline object of the
+dominant kernel and the fp64 CPU oracle timed on a bounded sample of the
+headline workload.
 """
 from __future__ import annotations
 
@@ -23,6 +32,7 @@ import argparse
 import json
 import math
 import os
+import platform
 import sys
 import time
 
@@ -35,6 +45,9 @@ METRIC = "fused norm+GEMM+SiLU TFLOP/s & % MFMA peak; decode GB/s & % HBM peak"
 PEAK_MFMA_F16_TFLOPS = 2516.6   # 256 CUs x 2.4 GHz x 4096 dense fp16/bf16 FLOP/clk/CU
 PEAK_HBM_GBS = 8000.0           # HBM3E, 8 TB/s
 LLC_BYTES = 256 << 20           # Infinity Cache (MALL)
+HEADLINE = "rms_matmul_silu_512x14336"
+EXTRAS = ("ffn_silu_512x14336x49152", "ln_linear_bias_1024x8192", "decode_rms_gemm_m1",
+          "decode_rms_gemm_m8", "decode_rms_gemm_m32", "ln_linear_bias_64x256")
 
 
 def workload(name: str):
@@ -58,7 +71,7 @@ def kernel_sources_sha() -> str:
 
 
 def recorded_traffic(workload_name: str):
-    """HBM bytes per launch measured with rocprofv3 (FETCH_SIZE and WRITE_SIZE,
+    """HBM bytes per step measured with rocprofv3 (FETCH_SIZE and WRITE_SIZE,
     scaled by a copy-kernel calibration), or None when no record exists for
     this workload or the kernels changed since it was taken."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
@@ -93,31 +106,19 @@ def algorithmic(case):
     return 2 * M * N * K, nbytes + M * N * 2
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    # The GPU clock ramps up over tens of milliseconds of sustained load: a
-    # few warmup steps would time part of the ramp rather than steady state.
-    ap.add_argument("--warmup", type=int, default=400)
-    ap.add_argument("--workload", default="ln_linear_bias_1024x8192")
-    ap.add_argument("--no-cpu-baseline", action="store_true",
-                    help="skip the oracle timing (e.g. under a profiler)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="target CPU time of the oracle sample")
-    args = ap.parse_args()
+def launches_per_step(case) -> int:
+    is_ffn = case.kind in ("ffn", "gated_ffn")
+    return (2 if is_ffn else 1) + (1 if case.norm and case.M > 32 else 0)
 
-    if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU: this build has no multi-GPU path "
-              f"(got --gpus {args.gpus}).", file=sys.stderr)
-        return 2
 
+def measure(name: str, steps: int, warmup: int):
+    """Time `steps` back-to-back steps of workload `name` after `warmup`
+    untimed ones; returns (case, result dict)."""
     import torch
     import norm_gemm_amd as ng
 
-    case = workload(args.workload)
+    case = workload(name)
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     A = case.arrays
     flops, nbytes = algorithmic(case)
     is_ffn = case.kind in ("ffn", "gated_ffn")
@@ -128,16 +129,13 @@ def main():
     wbytes = sum(A[k].size * 2 for k in wkeys)
     copies = max(2, math.ceil(1.5 * LLC_BYTES / wbytes) + 1)
     up = {k: upload(v, case.dtype, dev) for k, v in A.items() if v is not None and k not in wkeys}
-    wsets = []
     base = {k: upload(A[k], case.dtype, dev) for k in wkeys}
-    for c in range(copies):
-        wsets.append({k: (base[k] if c == 0 else base[k].clone()) for k in wkeys})
-    get = lambda k: up.get(k)
+    wsets = [{k: (base[k] if c == 0 else base[k].clone()) for k in wkeys} for c in range(copies)]
+    get = up.get
     out = torch.empty(case.M, case.N, dtype=up["x"].dtype, device=dev)
     ws = None
     if is_ffn:
-        ws = torch.empty(ws_size(case.M, case.F, up["x"].dtype),
-                         dtype=torch.uint8, device=dev)
+        ws = torch.empty(ws_size(case.M, case.F, up["x"].dtype), dtype=torch.uint8, device=dev)
 
     def step(i):
         w = wsets[i % copies]
@@ -149,89 +147,62 @@ def main():
             ng.fused_norm_gemm(get("x"), w["W"], get("gamma"), get("beta"), get("bias"),
                                eps=case.eps, norm=case.norm, act=case.act, out=out)
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
 
+    # K steps back to back between two events on the launch stream (per-step
+    # events would add their own gaps).
     stream = torch.cuda.current_stream(dev)
-    # Whole-job throughput: exactly K steps back to back between two events
-    # (per-step events would add their own gaps to the total).
-    t_all0, t_all1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    t_all0.record(stream)
-    for i in range(args.steps):
+    t0.record(stream)
+    for i in range(steps):
         step(i)
-    t_all1.record(stream)
+    t1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    total_ms = t_all0.elapsed_time(t_all1)
-    ms_per_step = total_ms / args.steps
-    # Per-launch durations for the roofline: a second pass of K steps, each
-    # bracketed by events on the stream the kernels run on.
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    for i in range(args.steps):
-        ev[i][0].record(stream)
-        step(i)
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    per_launch = np.array([a.elapsed_time(b) for a, b in ev])
-    avg_launch_ms = float(per_launch.mean())
+    ms_per_step = t0.elapsed_time(t1) / steps
 
     decode = case.M <= 32
     if decode:
         value = nbytes / (ms_per_step * 1e-3) / 1e9
-        unit = "GB/s"
-        achieved = nbytes / (avg_launch_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                "traffic": recorded_traffic(case.name)}
+        unit, bound, peak, runit = "GB/s", "hbm", PEAK_HBM_GBS, "GB/s"
     else:
         value = flops / (ms_per_step * 1e-3) / 1e12
-        unit = "TFLOP/s"
-        achieved = flops / (avg_launch_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_MFMA_F16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_MFMA_F16_TFLOPS, 4),
-                "traffic": recorded_traffic(case.name)}
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(case, args.cpu_seconds, decode)
-
-    line = {
-        "metric": METRIC,
+        unit, bound, peak, runit = "TFLOP/s", "mfma", PEAK_MFMA_F16_TFLOPS, "TFLOP/s"
+    res = {
+        "workload": case.name,
         "value": round(value, 2),
         "unit": unit,
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f16" if case.dtype == 0 else "bf16",
-        "data": "synthetic (seeded PCG64 normals; W rotated over %d device copies)" % copies,
-        "config": {"workload": case.name, "M": case.M, "K": case.K, "N": case.N,
-                   **({"F": case.F} if is_ffn else {}),
-                   "norm": ["none", "layernorm", "rmsnorm"][case.norm],
-                   "act": ["none", "silu", "relu", "gelu"][case.act], "gated": case.kind == "gated_ffn",
-                   "bias": (A.get("bias") is not None) or (A.get("b1") is not None),
-                   "eps": case.eps,
-                   "launches_per_step": (2 if is_ffn else 1) + (1 if case.norm and case.M > 32 else 0)},
-        "roofline": roof,
-        "cpu_baseline": cpu,
-        "timing": {"avg_launch_ms": round(avg_launch_ms, 5),
-                   "p10_launch_ms": round(float(np.percentile(per_launch, 10)), 5),
-                   "p50_launch_ms": round(float(np.percentile(per_launch, 50)), 5),
-                   "p90_launch_ms": round(float(np.percentile(per_launch, 90)), 5),
-                   "host_wall_s": round(wall, 4)},
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "steps": steps,
+        "warmup": warmup,
+        "launches_per_step": launches_per_step(case),
+        "roofline": {"bound": bound, "achieved": round(value, 1), "peak": peak, "unit": runit,
+                     "frac": round(value / peak, 4), "traffic": recorded_traffic(case.name)},
+        "host_wall_s": round(wall, 4),
+        "weight_copies": copies,
     }
-    print(json.dumps(line), flush=True)
-    return 0
+    del wsets, base, up, out, ws
+    torch.cuda.empty_cache()
+    return case, res
 
 
-def cpu_baseline(case, seconds: float, decode: bool):
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(case, seconds: float):
     """The fp64 oracle as it stands, on whole output rows of the workload,
     doubling the row count until about `seconds` of wall time are spent."""
     import oracle
@@ -249,18 +220,86 @@ def cpu_baseline(case, seconds: float, decode: bool):
         batch *= 2
     flops, nbytes = algorithmic(case)
     frac = done_rows / case.M
-    if decode:
+    if case.M <= 32:
         # the oracle streams all of W for every row, so its rate is reported
         # as the workload's algorithmic bytes scaled by the rows completed
-        value = nbytes * frac / spent / 1e9
-        unit = "GB/s"
+        value, unit = nbytes * frac / spent / 1e9, "GB/s"
     else:
-        value = flops * frac / spent / 1e12
-        unit = "TFLOP/s"
+        value, unit = flops * frac / spent / 1e12, "TFLOP/s"
     return {"value": round(value, 6), "unit": unit, "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": f"{done_rows} of {case.M} output rows (all {case.N} columns), "
-                      f"{spent:.1f} s, fp64"}
+            "sample": f"{done_rows} of {case.M} output rows (all {case.N} columns) of "
+                      f"{case.name}, {spent:.1f} s, fp64",
+            "cpu_model": cpu_model(), "compile_flags": " ".join(oracle.COMPILE_FLAGS)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    # The GPU clock ramps up over tens of milliseconds of sustained load.
+    ap.add_argument("--warmup", type=int, default=400)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--only", action="store_true",
+                    help="measure only --workload (no other workloads; e.g. under a profiler)")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle timing (e.g. under a profiler)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              f"(got --gpus {args.gpus}).", file=sys.stderr)
+        return 2
+
+    import torch
+    torch.cuda.set_device(0)
+
+    extras = []
+    if not args.only:
+        for name in EXTRAS:
+            if name == args.workload:
+                continue
+            _, r = measure(name, max(args.steps, 20), max(args.warmup, 100))
+            extras.append(r)
+            print(f"# {name}: {r['value']} {r['unit']} ({r['us_per_step']} us/step)",
+                  file=sys.stderr, flush=True)
+
+    case, main_res = measure(args.workload, args.steps, args.warmup)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(case, args.cpu_seconds)
+    A = case.arrays
+    is_ffn = case.kind in ("ffn", "gated_ffn")
+    line = {
+        "metric": METRIC,
+        "value": main_res["value"],
+        "unit": main_res["unit"],
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16" if case.dtype == 0 else "bf16",
+        "data": "synthetic (seeded PCG64 normals; W rotated over %d device copies)"
+                % main_res["weight_copies"],
+        "config": {"workload": case.name, "M": case.M, "K": case.K, "N": case.N,
+                   **({"F": case.F} if is_ffn else {}),
+                   "norm": ["none", "layernorm", "rmsnorm"][case.norm],
+                   "act": ["none", "silu", "relu", "gelu"][case.act],
+                   "gated": case.kind == "gated_ffn",
+                   "bias": (A.get("bias") is not None) or (A.get("b1") is not None),
+                   "eps": case.eps, "launches_per_step": main_res["launches_per_step"]},
+        "roofline": main_res["roofline"],
+        "cpu_baseline": cpu,
+        "timing": {"us_per_step": main_res["us_per_step"], "host_wall_s": main_res["host_wall_s"],
+                   "region": "K back-to-back steps between two events on the launch stream"},
+        "workloads": extras,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
 
 
 if __name__ == "__main__":

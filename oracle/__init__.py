@@ -28,12 +28,16 @@ NORM_NONE, NORM_LAYERNORM, NORM_RMSNORM = 0, 1, 2
 ACT_NONE, ACT_SILU, ACT_RELU, ACT_GELU = 0, 1, 2, 3
 
 
+# gcc flags of the oracle library: portable x86-64 code (it is built on one
+# host and may run on another), OpenMP over output elements.
+COMPILE_FLAGS = ("-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp")
+
+
 def build(force: bool = True) -> str:
     """Compile ``oracle.c`` with gcc (portable x86-64 code, OpenMP)."""
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp"
-        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
-               "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+        cmd = ["gcc", *COMPILE_FLAGS, "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB)
     return _LIB
