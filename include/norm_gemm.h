@@ -60,7 +60,8 @@
 extern "C" {
 #endif
 
-#define NORM_GEMM_ABI_VERSION 3   /* 2: NG_ACT_RELU, NG_ACT_GELU; 3: fused_gated_ffn */
+#define NORM_GEMM_ABI_VERSION 4   /* 2: NG_ACT_RELU, NG_ACT_GELU; 3: fused_gated_ffn;
+                                     4: fused_ffn_noalloc, NG_ERR_SCRATCH */
 
 typedef enum { NG_NORM_NONE = 0, NG_NORM_LAYERNORM = 1, NG_NORM_RMSNORM = 2 } ng_norm_t;
 typedef enum { NG_ACT_NONE = 0, NG_ACT_SILU = 1, NG_ACT_RELU = 2, NG_ACT_GELU = 3 } ng_act_t;
@@ -76,7 +77,8 @@ typedef enum {
     NG_ERR_WORKSPACE = -6,    /* workspace missing or smaller than required       */
     NG_ERR_UNSUPPORTED = -7,  /* no kernel for this request                       */
     NG_ERR_ALIGN = -8,        /* a pointer is not 2-byte aligned                  */
-    NG_ERR_HIP = -9           /* the HIP runtime reported an error                */
+    NG_ERR_HIP = -9,          /* the HIP runtime reported an error                */
+    NG_ERR_SCRATCH = -10      /* fused_ffn_noalloc: workspace beyond its scratch   */
 } ng_status_t;
 
 /*
@@ -151,6 +153,30 @@ int fused_gated_ffn(const void *x, const void *gamma, const void *beta,
                     void *y, int64_t M, int64_t K, int64_t F, int64_t N,
                     float eps, int norm, int act, int dtype,
                     void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * fused_ffn_noalloc: fused_ffn for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation). Same arguments, results and kernels as fused_ffn, without the
+ * workspace: h (and, when they fit, the split-K partial sums of y) live in a
+ * static device array of NG_FFN_NOALLOC_SCRATCH_BYTES bytes that the library
+ * holds on each device it runs on until the process ends. The call allocates
+ * nothing and calls no allocating routine; its output equals fused_ffn's
+ * with a 256-byte aligned workspace of NG_FFN_NOALLOC_SCRATCH_BYTES bytes.
+ * Requests whose h exceeds the array (M * F * 2 bytes, rounded up to 256, >
+ * NG_FFN_NOALLOC_SCRATCH_BYTES) return NG_ERR_SCRATCH, checked before any
+ * HIP call. All calls on one device share its array: calls that overlap in
+ * time on one device (different streams, or threads with no ordering
+ * between them) race and give wrong results; calls ordered on one stream are
+ * safe. Nothing in the array needs to start at zero (every byte a call
+ * reads, it wrote first). Returns an ng_status_t.
+ */
+#define NG_FFN_NOALLOC_SCRATCH_BYTES (64u << 20) /* 64 MiB per device */
+
+int fused_ffn_noalloc(const void *x, const void *gamma, const void *beta,
+                      const void *W1, const void *b1, const void *W2, const void *b2,
+                      void *y, int64_t M, int64_t K, int64_t F, int64_t N,
+                      float eps, int norm, int act, int dtype, void *stream);
 
 /* Human-readable text of a status code (static storage, never NULL). */
 const char *norm_gemm_status_string(int status);

@@ -6,6 +6,7 @@ supplies device memory and the stream. The functions mirror the C ABI in
 
 * :func:`fused_norm_gemm` -- y = act(norm_affine(x) @ W.T + bias)
 * :func:`fused_ffn` -- y = act(norm_affine(x) @ W1.T + b1) @ W2.T + b2
+* :func:`fused_ffn_noalloc` -- the FFN with the library's static workspace
 * :func:`fused_ffn_workspace_size`, :func:`norm_gemm_status_string`,
   :func:`norm_gemm_abi_version`
 
@@ -31,7 +32,12 @@ DTYPES = {torch.float16: 0, torch.bfloat16: 1}
 
 # Symbols declared in include/norm_gemm.h.
 EXPORTED = ("fused_norm_gemm", "fused_ffn", "fused_ffn_workspace_size", "fused_gated_ffn",
-            "fused_gated_ffn_workspace_size", "norm_gemm_status_string", "norm_gemm_abi_version")
+            "fused_gated_ffn_workspace_size", "fused_ffn_noalloc", "norm_gemm_status_string",
+            "norm_gemm_abi_version")
+
+# Size of the static device array behind fused_ffn_noalloc
+# (NG_FFN_NOALLOC_SCRATCH_BYTES in include/norm_gemm.h).
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class NormGemmError(RuntimeError):
@@ -56,6 +62,9 @@ def _load() -> ctypes.CDLL:
     L.fused_gated_ffn_workspace_size.restype = sz
     L.fused_gated_ffn.argtypes = L.fused_ffn.argtypes
     L.fused_gated_ffn.restype = ci
+    L.fused_ffn_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, f32, ci,
+                                    ci, ci, vp]
+    L.fused_ffn_noalloc.restype = ci
     L.norm_gemm_status_string.argtypes = [ci]
     L.norm_gemm_status_string.restype = ctypes.c_char_p
     L.norm_gemm_abi_version.argtypes = []
@@ -183,8 +192,22 @@ def fused_gated_ffn(x: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor,
     return _ffn(True, x, w1, w2, gamma, beta, b1, b2, eps, norm, act, workspace, out, stream)
 
 
-def _ffn(gated, x, w1, w2, gamma, beta, b1, b2, eps, norm, act, workspace, out, stream):
-    what = "fused_gated_ffn" if gated else "fused_ffn"
+def fused_ffn_noalloc(x: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor,
+                      gamma: Optional[torch.Tensor] = None, beta: Optional[torch.Tensor] = None,
+                      b1: Optional[torch.Tensor] = None, b2: Optional[torch.Tensor] = None, *,
+                      eps: float = 1e-5, norm="none", act="silu",
+                      out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """:func:`fused_ffn` whose intermediate lives in the library's static
+    per-device array (:data:`NOALLOC_SCRATCH_BYTES`): the library call
+    allocates nothing. Pass ``out`` to keep this function free of
+    allocations too. Calls that overlap in time on one device race."""
+    return _ffn(False, x, w1, w2, gamma, beta, b1, b2, eps, norm, act, None, out, stream,
+                noalloc=True)
+
+
+def _ffn(gated, x, w1, w2, gamma, beta, b1, b2, eps, norm, act, workspace, out, stream,
+         noalloc=False):
+    what = "fused_gated_ffn" if gated else ("fused_ffn_noalloc" if noalloc else "fused_ffn")
     if not isinstance(x, torch.Tensor) or x.dim() < 1:
         raise ValueError("x must be a tensor with at least one dimension")
     if x.dtype not in DTYPES:
@@ -201,22 +224,26 @@ def _ffn(gated, x, w1, w2, gamma, beta, b1, b2, eps, norm, act, workspace, out, 
     for t, name, shp in ((x, "x", None), (w1, "w1", None), (w2, "w2", None), (gamma, "gamma", (K,)),
                          (beta, "beta", (K,)), (b1, "b1", (w1.shape[0],)), (b2, "b2", (N,))):
         _check(t, name, x.dtype, dev, shp)
-    need = (fused_gated_ffn_workspace_size if gated else fused_ffn_workspace_size)(M, F, x.dtype)
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    if workspace.device != dev or not workspace.is_contiguous():
-        raise ValueError("workspace must be a contiguous tensor on x's device")
+    if not noalloc:
+        need = (fused_gated_ffn_workspace_size if gated else fused_ffn_workspace_size)(M, F, x.dtype)
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        if workspace.device != dev or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on x's device")
     lead = tuple(x.shape[:-1])
     if out is None:
         out = torch.empty(lead + (N,), dtype=x.dtype, device=dev)
     _check(out, "out", x.dtype, dev, lead + (N,))
-    ws_bytes = workspace.numel() * workspace.element_size()
     with torch.cuda.device(dev):
-        fn = lib.fused_gated_ffn if gated else lib.fused_ffn
-        st = fn(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(w1), _ptr(b1), _ptr(w2),
-                _ptr(b2), _ptr(out), M, K, F, N, float(eps),
-                _enum(NORMS, norm, "norm"), _enum(ACTS, act, "act"),
-                DTYPES[x.dtype], _ptr(workspace), ws_bytes, _stream(dev, stream))
+        common = (_ptr(x), _ptr(gamma), _ptr(beta), _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2),
+                  _ptr(out), M, K, F, N, float(eps), _enum(NORMS, norm, "norm"),
+                  _enum(ACTS, act, "act"), DTYPES[x.dtype])
+        if noalloc:
+            st = lib.fused_ffn_noalloc(*common, _stream(dev, stream))
+        else:
+            fn = lib.fused_gated_ffn if gated else lib.fused_ffn
+            ws_bytes = workspace.numel() * workspace.element_size()
+            st = fn(*common, _ptr(workspace), ws_bytes, _stream(dev, stream))
     if st != 0:
         raise NormGemmError(st, what)
     return out

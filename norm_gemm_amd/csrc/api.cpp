@@ -11,6 +11,31 @@
 
 namespace ng {
 
+// Workspace of fused_ffn_noalloc: one array per device, held until the
+// process ends. Host code never uses this name as an address (in host code it
+// is a stand-in symbol); it uses the device address that scratch_ptr() takes
+// once per device with hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[NG_FFN_NOALLOC_SCRATCH_BYTES];
+
+// Device address of this device's scratch array, taken on the device's first
+// call with that device current, or nullptr when the query fails.
+void *scratch_ptr()
+{
+    constexpr int kMaxDev = 64;
+    static std::atomic<void *> ptrs[kMaxDev];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev)
+        return nullptr;
+    void *p = ptrs[dev].load(std::memory_order_acquire);
+    if (p)
+        return p;
+    void *q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q)
+        return nullptr;
+    ptrs[dev].store(q, std::memory_order_release);
+    return q;
+}
+
 int cu_count()
 {
     // one entry per device ordinal; filled on first use, read-only after
@@ -132,6 +157,26 @@ int fused_ffn(const void *x, const void *gamma, const void *beta, const void *W1
     return ffn_down(workspace, W2, b2, y, M, F, N, dtype, workspace, workspace_bytes, s);
 }
 
+int fused_ffn_noalloc(const void *x, const void *gamma, const void *beta, const void *W1,
+                      const void *b1, const void *W2, const void *b2, void *y, int64_t M,
+                      int64_t K, int64_t F, int64_t N, float eps, int norm, int act, int dtype,
+                      void *stream)
+{
+    // every argument check that needs no device first: with no workspace
+    // the FFN validation fails last, on the workspace, if all else is valid
+    int st = ng_validate_ffn(x, gamma, beta, W1, b1, W2, b2, y, M, K, F, N, eps, norm, act,
+                             dtype, nullptr, 0);
+    if (st != NG_ERR_WORKSPACE)
+        return st == NG_OK ? NG_ERR_WORKSPACE : st;
+    if (ng_ffn_workspace_size(M, F, dtype) > (size_t)NG_FFN_NOALLOC_SCRATCH_BYTES)
+        return NG_ERR_SCRATCH;
+    void *ws = ng::scratch_ptr();
+    if (!ws)
+        return NG_ERR_HIP;
+    return fused_ffn(x, gamma, beta, W1, b1, W2, b2, y, M, K, F, N, eps, norm, act, dtype, ws,
+                     (size_t)NG_FFN_NOALLOC_SCRATCH_BYTES, stream);
+}
+
 size_t fused_gated_ffn_workspace_size(int64_t M, int64_t F, int dtype)
 {
     return ng_gated_ffn_workspace_size(M, F, dtype);
@@ -181,6 +226,10 @@ const char *norm_gemm_status_string(int status)
     case NG_ERR_UNSUPPORTED: return "unsupported request";
     case NG_ERR_ALIGN: return "a pointer is not 2-byte aligned";
     case NG_ERR_HIP: return "HIP runtime error";
+    case NG_ERR_SCRATCH:
+        return "the request needs more workspace than the allocation-free entry point's "
+               "static scratch holds (M * F * 2 bytes, rounded up to 256, at most "
+               "NG_FFN_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
     }
 }

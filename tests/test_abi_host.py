@@ -14,7 +14,8 @@ import norm_gemm_amd as ng
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "norm_gemm.h")
 
-OK, NULL, SHAPE, ENUM, EPS, ALIAS, WORKSPACE, UNSUP, ALIGN, HIP = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
+OK, NULL, SHAPE, ENUM, EPS, ALIAS, WORKSPACE, UNSUP, ALIGN, HIP, SCRATCH = \
+    0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10
 
 # Fake device addresses: validation compares them as integers and never
 # dereferences them; each failing call returns before any HIP call. Where a
@@ -48,8 +49,8 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert ng.norm_gemm_abi_version() == 3
-    for s in (OK, NULL, SHAPE, ENUM, EPS, ALIAS, WORKSPACE, UNSUP, ALIGN, HIP):
+    assert ng.norm_gemm_abi_version() == 4
+    for s in (OK, NULL, SHAPE, ENUM, EPS, ALIAS, WORKSPACE, UNSUP, ALIGN, HIP, SCRATCH):
         assert ng.norm_gemm_status_string(s)
     assert ng.norm_gemm_status_string(12345) == "unknown status"
 
@@ -150,3 +151,28 @@ def test_python_binding_rejects_cpu_tensors():
         ng.fused_norm_gemm(x, w)
     with pytest.raises(ValueError):
         ng.fused_norm_gemm(x.float(), w)
+
+
+def ffn_noalloc(x=X, g=G, b=B, w1=W, b1=BI, w2=0x90000000, b2=0xA0000000, y=Y, M=4, K=16, F=32,
+                N=8, eps=1e-5, norm=1, act=1, dtype=0):
+    return ng.lib.fused_ffn_noalloc(x, g, b, w1, b1, w2, b2, y, M, K, F, N, eps, norm, act, dtype,
+                                    None)
+
+
+# Every status below is returned before any HIP call (argument checks, then
+# the scratch size), so these run only where no GPU is visible.
+@pytest.mark.parametrize("kw,status", [
+    (dict(w2=None), NULL), (dict(act=9), ENUM), (dict(F=0), SHAPE), (dict(eps=-1.0), EPS),
+    (dict(y=X + 1), ALIGN), (dict(y=0x90000000), ALIAS),
+    # h = M F 2 bytes: 64 MiB + 256 bytes is one 256-byte block past the array
+    (dict(M=512, F=65536 + 1, K=16), SCRATCH),
+])
+@no_gpu_only
+def test_fused_ffn_noalloc_validation_errors(kw, status):
+    assert ffn_noalloc(**kw) == status
+
+
+def test_noalloc_scratch_size_matches_the_header():
+    text = open(HEADER, encoding="utf-8").read()
+    assert "#define NG_FFN_NOALLOC_SCRATCH_BYTES (64u << 20)" in text
+    assert ng.NOALLOC_SCRATCH_BYTES == 64 << 20
