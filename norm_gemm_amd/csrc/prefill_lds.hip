@@ -109,7 +109,9 @@ __device__ __forceinline__ void tile_of(const TileMap &mp, int b, int &mb, int &
 }
 
 // Statistics modes of the main kernel.
-enum { ST_NONE = 0, ST_PROLOGUE = 1, ST_FROM_Y = 2 };
+// ST_FROM_Y_PS: statistics from y, fp16 RMSNorm without beta, power-of-two
+// prescaled operand (see the kernel).
+enum { ST_NONE = 0, ST_PROLOGUE = 1, ST_FROM_Y = 2, ST_FROM_Y_PS = 3 };
 
 // Row-statistics pass for ST_FROM_Y: one wave per row of x, one pass over the
 // row with 128-bit loads and packed dot products accumulating in fp32, a wave
@@ -167,14 +169,30 @@ __global__ __launch_bounds__(256) void row_stats_to_y_kernel(const uint16_t *__r
 }
 
 // GB: bit 0 gamma present, bit 1 beta present (with STATS != ST_NONE);
-// KT: K % 64 != 0 (the last K step is ragged); LN: LayerNorm (else RMSNorm,
-// with STATS != ST_NONE); GT: gated output (see the gated epilogue): W is
-// [2N, K] = [W_gate; W_up], bias [2N], and a tile covers 128 output columns;
-// SK: split K (no normalization): workgroup b computes tile b % T over the
-// b / T-th of ksplit contiguous K ranges and writes its fp32 partial sums to
-// part[b / T][M][N] (bias and activation are applied by the sum of the
-// partials).
-template <int DT, int STATS, int GB, bool KT, bool LN, bool GT, bool SK>
+// KT: K % 64 != 0 (the last K step is ragged); GT: gated output (see the
+// gated epilogue): W is [2N, K] = [W_gate; W_up], bias [2N], and a tile
+// covers 128 output columns; SK: split K (no normalization): workgroup b
+// computes tile b % T over the b / T-th of ksplit contiguous K ranges and
+// writes its fp32 partial sums to part[b / T][M][N] (bias and activation are
+// applied by the sum of the partials). norm selects LayerNorm or RMSNorm for
+// the in-kernel statistics (STATS == ST_PROLOGUE).
+//
+// Schedule ("ping-pong"). Waves w and w + 4 of a workgroup run on the same
+// SIMD (workgroups are dealt to SIMDs that way), and the two groups of four
+// waves alternate between two phases separated by workgroup barriers:
+//   memory phase of step kt: read all of this wave's MFMA fragments of step
+//     kt from LDS into registers; issue the direct loads of step kt + 2;
+//     once the loads of step kt + 1 have landed, normalize this wave's x
+//     chunks of step kt + 1 into their stage and issue the x loads of step
+//     kt + 2 into the same registers;
+//   compute phase of step kt: the 16 MFMAs of step kt, back to back.
+// Waves 4-7 start one phase later, so while one wave of a SIMD runs its
+// MFMAs the other runs its memory phase (LDS reads, loads, VALU work), and
+// the matrix core of every SIMD always has a wave with operands ready. Each
+// stage is read by the first group in phase 2 kt and by the second in phase
+// 2 kt + 1, so a stage is rewritten (direct loads of kt + 3, normalized x of
+// kt + 3) only from phase 2 kt + 2 on.
+template <int DT, int STATS, int GB, bool KT, bool GT, bool SK>
 __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ gamma,
     const uint16_t *__restrict__ beta, const uint16_t *__restrict__ W,
@@ -183,6 +201,16 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
 {
     static_assert(!SK || (STATS == ST_NONE && !GT), "split K only for the plain GEMM");
     constexpr bool AFFINE = STATS != ST_NONE;
+    // Prescaled fp16 RMSNorm (no beta): the A operand is x * 2^e * gamma,
+    // rounded once to fp16, with 2^e the power of two at or below the row's
+    // rs = 1/sqrt(mean(x^2) + eps) (e clamped to the fp16 normal exponents
+    // -14..15, so 2^e is an fp16 value and x * 2^e is exact). The epilogue
+    // multiplies the fp32 sum by rs * 2^-e, which is exact scaling of the
+    // same sum: y = rs 2^-e sum_k fp16(x_k 2^e gamma_k) W_k. Two packed fp16
+    // products per two elements replace the fp32 normalization, and the
+    // operand values keep the range of the normalized row (|x 2^e| <= |x rs|).
+    constexpr bool PS = STATS == ST_FROM_Y_PS;
+    static_assert(!PS || (DT == DT_F16 && !(GB & 2)), "prescale: fp16 without beta");
     constexpr bool HG = AFFINE && (GB & 1), HB = AFFINE && (GB & 2);
     // direct loads per lane per K step: W, plus x when it is not normalized
     // (normalized x, gamma and beta come through registers)
@@ -191,9 +219,6 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
     // One LDS object per pipeline stage and operand
     __shared__ u32x4 A0[A_TILE], A1[A_TILE], A2[A_TILE];
     __shared__ u32x4 B0[B_TILE], B1[B_TILE], B2[B_TILE];
-    // gamma (chunks 0-7) and beta (chunks 8-15) of one K step, in three slots
-    // used like the stages (see the K step); one chunk per lane of a wave
-    __shared__ u32x4 G0[64], G1[64], G2[64];
     auto Ast = [&](auto sc) -> u32x4 * {
         constexpr int i = decltype(sc)::value % NSTAGE;
         if constexpr (i == 0)
@@ -212,22 +237,13 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
         else
             return B2;
     };
-    auto Gst = [&](auto sc) -> u32x4 * {
-        constexpr int i = decltype(sc)::value % NSTAGE;
-        if constexpr (i == 0)
-            return G0;
-        else if constexpr (i == 1)
-            return G1;
-        else
-            return G2;
-    };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave / WGN, wn = wave % WGN;
+    const int wm = wave / WGN, wn = wave % WGN;   // wm is also the phase group
     const int lrow = lane & 31, lk = lane >> 5;
     // K range of this workgroup: all of K, or with split K the ks-th of
     // ksplit ranges of whole K steps (the host gives every range a step).
@@ -237,7 +253,6 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
     const int kbase = SK ? ks * nks * BK : 0;
     const int Ke = SK ? min(K - kbase, nks * BK) : K;
     const int nk = (Ke + BK - 1) / BK;
-    constexpr bool k_tail = KT;
 
     // output columns per tile: 256, or 128 gated (the 256 W rows of a tile are
     // the gate and up rows of the same 128 columns)
@@ -253,11 +268,11 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
     // when normalized, W rows' outputs are discarded); steps past the last
     // re-read the last step (never consumed).
     // Addressing: a uniform base (tile origin + K step, scalar registers)
-    // plus a per-lane 32-bit byte offset that is fixed for the whole tile, so
-    // no address register is rewritten while its load is in flight (the
-    // compiler would wait for the load before reusing it). The last K step
-    // of a ragged K has its own fixed offsets: chunks past K re-read the
-    // row's last valid chunk (in bounds) and are zeroed once landed.
+    // plus a per-lane 32-bit byte offset that is fixed for the whole tile
+    // (the host routes shapes whose offsets would reach 2^32 elsewhere), so
+    // no address register is rewritten while its load is in flight. The last
+    // K step of a ragged K has its own fixed offsets: chunks past K re-read
+    // the row's last valid chunk (in bounds) and are zeroed once landed.
     const int kl = (nk - 1) * BK;                     // first k of the last step
     const int clast = (Ke - kl + 7) / 8 - 1;          // last valid chunk in it
     auto tail_chunk = [&](int c) { return kl + c * 8 < Ke ? c : clast; };
@@ -296,7 +311,7 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
     }
     // gamma / beta chunk of this lane's x chunks (tail: clamped in bounds)
     const uint32_t goff = ach[0] * 16u, goff_t = tail_chunk(ach[0]) * 16u;
-    auto issue = [&](int kt, u32x4 *As, u32x4 *Bs) {
+    auto issue_dma = [&](int kt, u32x4 *As, u32x4 *Bs) {
         kt = min(kt, nk - 1);
         const bool tl = KT && kt == nk - 1;
         const char *wb = reinterpret_cast<const char *>(wtile) + (size_t)kt * (BK * 2);
@@ -311,14 +326,27 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
             dma16(wb, tl ? woff_t[i] : woff[i], lds_addr(&Bs[(wave * B_RPW + i * 8) * CPR]));
     };
 
-    // (rs, nmr) of the rows of this lane's x chunks
+    // (rs, nmr) of the rows of this lane's x chunks: normalized = x rs + nmr
     float rrs[A_DMA], rnmr[A_DMA];
 #pragma unroll
     for (int i = 0; i < A_DMA; ++i) {
         rrs[i] = 1.0f;
         rnmr[i] = 0.0f;
     }
-    if constexpr (STATS == ST_FROM_Y) {
+    // prescale: 2^e of this lane's x rows (packed fp16) and rs 2^-e of the
+    // output rows of its accumulators (rows wm * 64 + 32 i + lrow)
+    half2_t ps2[A_DMA];
+    float osc[FM];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+        osc[i] = 1.0f;
+    auto pow2_below = [](float rs) {
+        // 2^e <= rs, e = floor(log2 rs) clamped to -14..15 (rs > 0, finite)
+        int e = (int)((__builtin_bit_cast(uint32_t, rs) >> 23) & 0xffu) - 127;
+        e = e < -14 ? -14 : (e > 15 ? 15 : e);
+        return __builtin_bit_cast(float, (uint32_t)(e + 127) << 23);
+    };
+    if constexpr (STATS == ST_FROM_Y || PS) {
         // statistics left by the statistics pass in this tile's own rows
 #pragma unroll
         for (int i = 0; i < A_DMA; ++i) {
@@ -327,15 +355,31 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
             rrs[i] = __builtin_bit_cast(float, pk.x);
             rnmr[i] = __builtin_bit_cast(float, pk.y);
         }
+        if constexpr (PS) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int m = min(m0 + wm * WM + i * 32 + lrow, M - 1);
+                const float rs = __builtin_bit_cast(
+                    float, *reinterpret_cast<const uint32_t *>(y + (int64_t)m * N + n0));
+                osc[i] = rs / pow2_below(rs);
+            }
+        }
         // complete them before the direct loads start: the compiler does not
         // count those, so only an empty queue tells it these have landed
         wait_vmcnt<0>();
+        if constexpr (PS) {
+#pragma unroll
+            for (int i = 0; i < A_DMA; ++i) {
+                const _Float16 sh = (_Float16)pow2_below(rrs[i]);
+                ps2[i] = half2_t{sh, sh};
+            }
+        }
     } else if constexpr (STATS == ST_PROLOGUE) {
         // one wave per row, 4 rows at a time, reduced in fp32; exchanged
         // through the third x stage (not loaded before the first K step)
         float *s_rs = reinterpret_cast<float *>(A2);
         float *s_nmr = s_rs + BM;
-        const bool ln = LN;
+        const bool ln = norm == NORM_LAYERNORM;
         const int nch = K / 8;
         for (int rr = wave * (BM / NWAVE); rr < (wave + 1) * (BM / NWAVE); rr += 4) {
             float s1[4] = {0.f, 0.f, 0.f, 0.f}, s2[4] = {0.f, 0.f, 0.f, 0.f};
@@ -383,33 +427,20 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
         __syncthreads();
     }
 
-    // x chunks of K step kt that this lane loaded: normalized + affine in
-    // fp32, x * rs + nmr, then * gamma + beta, rounded once to the operand
-    // type (fp16: mixed-precision FMAs read the fp16 inputs directly and the
-    // last one rounds to fp16), written back in place; rows past M and chunks past K become
-    // zero. A lane's x rows are A_IST apart: one swizzle, so one logical
-    // chunk and one gamma / beta chunk for all of them. Split into the LDS
-    // reads and the arithmetic + write so that MFMAs can run in between.
+    // x chunks of one K step that this lane loads, with its gamma / beta
+    // chunk: loaded asynchronously into registers (ldg16_async), completed by
+    // wait_vmcnt_tied, then normalized + affine in fp32, x * rs + nmr, then
+    // * gamma + beta, rounded once to the operand type (fp16: mixed-precision
+    // FMAs read the fp16 inputs directly and the last one rounds to fp16),
+    // and written once into the step's stage; rows past M and chunks past K
+    // become zero. A lane's x rows are A_IST apart: one swizzle, so one
+    // logical chunk and one gamma / beta chunk for all of them.
     struct NormRaw {
         u32x4 v[A_DMA], g, b;
     };
-    // x / gamma / beta chunks of K step kt into registers (asynchronous: see
-    // ldg16_async; NXL loads, completed by wait_vmcnt_tied)
-    constexpr int NXL = A_DMA + (HG ? 1 : 0) + (HB ? 1 : 0);
-    // With both gamma and beta they come through LDS slots (issue_gb), read
-    // at the start of the step before the one that uses them; with one of
-    // them, straight into registers with x (measured faster there).
-    constexpr bool RING = HG && HB;
-    auto load_gb_regs = [&](int kt, NormRaw &r) {
-        kt = min(kt, nk - 1);
-        const bool tl = KT && kt == nk - 1;
-        const char *gb = reinterpret_cast<const char *>(gamma) + (size_t)kt * (BK * 2);
-        const char *bb = reinterpret_cast<const char *>(beta) + (size_t)kt * (BK * 2);
-        if constexpr (HG)
-            r.g = ldg16_async(gb, tl ? goff_t : goff);
-        if constexpr (HB)
-            r.b = ldg16_async(bb, tl ? goff_t : goff);
-    };
+    // two register buffers: the x chunks of step kt go to buffer kt % 2 and
+    // are loaded two steps before they are normalized
+    NormRaw raw[2];
     auto load_raw = [&](int kt, NormRaw &r) {
         kt = min(kt, nk - 1);
         const bool tl = KT && kt == nk - 1;
@@ -417,62 +448,61 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
 #pragma unroll
         for (int i = 0; i < A_DMA; ++i)
             r.v[i] = ldg16_async(xb, tl ? aoff_t[i] : aoff_g[i]);
-        r.g = r.b = u32x4{0u, 0u, 0u, 0u};
-        if constexpr (!RING)
-            load_gb_regs(kt, r);
+        const char *gb = reinterpret_cast<const char *>(gamma) + (size_t)kt * (BK * 2);
+        const char *bb = reinterpret_cast<const char *>(beta) + (size_t)kt * (BK * 2);
+        if constexpr (HG)
+            r.g = ldg16_async(gb, tl ? goff_t : goff);
+        else
+            r.g = u32x4{0u, 0u, 0u, 0u};
+        if constexpr (HB)
+            r.b = ldg16_async(bb, tl ? goff_t : goff);
+        else
+            r.b = u32x4{0u, 0u, 0u, 0u};
     };
-    // gamma / beta of K step kt into a slot: one direct load by wave 0 alone,
-    // lanes 0-7 the gamma chunks and 8-15 the beta chunks (past K: the last
-    // valid chunk; the other lanes repeat them). All waves of all CUs loading
-    // the same two lines every step would queue their requests at one L2
-    // channel; this is one request per line per CU and step. Issued two steps
-    // ahead: wave 0's waits on its x loads of the same step cover it, and the
-    // step's barrier publishes it.
-    auto issue_gb = [&](int kt, u32x4 *Gs) {
-        if constexpr (RING) {
-            if (wave == 0) {
-                kt = min(kt, nk - 1);
-                const int c = lane & 7;
-                const int k = (kt * BK + c * 8 < K) ? kt * BK + c * 8 : kl + clast * 8;
-                dma16_ptr(((lane & 8) == 0 ? gamma : beta) + k, lds_addr(Gs));
+    // one of this lane's x chunks of step kt
+    auto nrm_chunk = [&](int kt, u32x4 *As, const NormRaw &r, int i) {
+        const bool live = alive[i] && kt * BK + ach[0] * 8 < Ke;
+        if constexpr (PS) {
+            u32x4 v = r.v[i];
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                // copy the elements first (bit_cast of a vector element
+                // reference is miscompiled)
+                const uint32_t xw = v[d], gw = r.g[d];
+                half2_t t = __builtin_bit_cast(half2_t, xw) * ps2[i];   // exact
+                if constexpr (HG)
+                    t = t * __builtin_bit_cast(half2_t, gw);            // one rounding
+                v[d] = __builtin_bit_cast(uint32_t, t);
             }
+            As[(i * A_IST + wave * 8) * CPR + lane] = live ? v : u32x4{0u, 0u, 0u, 0u};
+            return;
         }
-    };
-    // (only with RING: otherwise the slots are never written and gamma / beta
-    // came into registers with x)
-    auto read_gb = [&](const u32x4 *Gs, NormRaw &r) {
-        if constexpr (RING) {
-            r.g = Gs[ach[0]];
-            r.b = Gs[CPR + ach[0]];
-        }
-    };
-    auto nrm_store = [&](int kt, u32x4 *As, const NormRaw &r) {
-        const bool kin = kt * BK + ach[0] * 8 < K;
         float g[8], bt[8];
         if constexpr (HG)
             unpack8<DT>(r.g, g);
         if constexpr (HB)
             unpack8<DT>(r.b, bt);
+        float f[8];
+        unpack8<DT>(r.v[i], f);
 #pragma unroll
-        for (int i = 0; i < A_DMA; ++i) {
-            const bool live = alive[i] && kin;
-            float f[8];
-            unpack8<DT>(r.v[i], f);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float v = fmaf(f[e], rrs[i], rnmr[i]);
-                if constexpr (HG && HB)
-                    f[e] = fmaf(v, g[e], bt[e]);
-                else if constexpr (HG)
-                    f[e] = v * g[e];
-                else if constexpr (HB)
-                    f[e] = v + bt[e];
-                else
-                    f[e] = v;
-            }
-            As[(i * A_IST + wave * 8) * CPR + lane] =
-                live ? pack8<DT>(f) : u32x4{0u, 0u, 0u, 0u};
+        for (int e = 0; e < 8; ++e) {
+            const float v = fmaf(f[e], rrs[i], rnmr[i]);
+            if constexpr (HG && HB)
+                f[e] = fmaf(v, g[e], bt[e]);
+            else if constexpr (HG)
+                f[e] = v * g[e];
+            else if constexpr (HB)
+                f[e] = v + bt[e];
+            else
+                f[e] = v;
         }
+        const u32x4 pk = pack8<DT>(f);
+        As[(i * A_IST + wave * 8) * CPR + lane] = live ? pk : u32x4{0u, 0u, 0u, 0u};
+    };
+    auto nrm_store = [&](int kt, u32x4 *As, const NormRaw &r) {
+#pragma unroll
+        for (int i = 0; i < A_DMA; ++i)
+            nrm_chunk(kt, As, r, i);
     };
     // without normalization only the chunks past K of the last step need
     // zeroing (rows past M re-read row M - 1 and their outputs are dropped)
@@ -491,32 +521,90 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
                 Bs[row * CPR + (lane & 7)] = u32x4{0u, 0u, 0u, 0u};
         }
     };
+    auto sb = [] { __builtin_amdgcn_sched_barrier(0); };
+    // plain workgroup barrier of the compute phase (no LDS access to wait for)
+    auto phase_barrier = [&] {
+        sb();
+        asm volatile("s_barrier" ::: "memory");
+        sb();
+    };
 
-    // ---- prologue: K steps 0 and 1 in flight; step 0 normalized
+    // ---- load order and waits. Loads complete in issue order, so a wait
+    // for one load is a wait for every older one; the orders below let each
+    // wait name only what is due (NXL = x / gamma / beta register loads of a
+    // step, LPS = direct loads of a step). The normalization runs in the
+    // compute phases, between a wave's own MFMAs, so that the memory phase
+    // (the one on the LDS) holds only fragment reads and load issue:
+    //   group 0: memory phase kt issues x of kt + 2, then the direct loads of
+    //            kt + 2; compute phase kt normalizes x of kt + 1 into its
+    //            stage and ends by awaiting the direct loads of kt + 1;
+    //   group 1: memory phase kt issues x of kt + 3 and awaits the direct
+    //            loads of kt + 1; compute phase kt starts with the direct
+    //            loads of kt + 3 (their stage was last read in the phase
+    //            before) and normalizes x of kt + 2 into its stage.
+    // Every stage is complete one barrier before the first group reads it;
+    // x gets three phases to arrive, the direct loads three to four.
+    constexpr int NXL = AFFINE ? A_DMA + (HG ? 1 : 0) + (HB ? 1 : 0) : 0;
+    auto tied_wait = [&](auto nc, NormRaw &r) {
+        wait_vmcnt_tied<decltype(nc)::value>(r.v[0], r.v[1], r.g, r.b);
+    };
+    using C0 = std::integral_constant<int, 0>;
+    using CX = std::integral_constant<int, NXL + 2 * LPS>;    // x of the step due
+    constexpr int CL = NXL + LPS;                             // group 0: loads of kt + 1
+    constexpr int CW = 2 * NXL + LPS;                         // group 1: loads of kt + 1
+
+    // ---- prologue: step 0 complete in its stage, the loads of steps 1-2
+    // in flight in each group's steady-state order. The x chunks of step j
+    // go to register buffer j % 2 in group 0 and (j + 1) % 2 in group 1, so
+    // that in every K step both groups load into buffer kt % 2 and
+    // normalize from the other one.
     issue_fence(x, gamma, beta);
     if constexpr (AFFINE) {
-        NormRaw r0;
-        load_raw(0, r0);
-        if constexpr (RING)
-            load_gb_regs(0, r0);
-        issue_gb(1, G1);
-        issue(0, A0, B0);
-        issue(1, A1, B1);
-        wait_vmcnt_tied<2 * LPS>(r0.v[0], r0.v[1], r0.g, r0.b);
-        nrm_store(0, A0, r0);
+        if (wm == 0) {
+            load_raw(0, raw[0]);
+            issue_dma(0, A0, B0);
+            load_raw(1, raw[1]);
+            issue_dma(1, A1, B1);
+            tied_wait(std::integral_constant<int, NXL + 2 * LPS>{}, raw[0]);
+            nrm_store(0, A0, raw[0]);
+            issue_fence(x, gamma, beta);
+            wait_vmcnt<NXL + LPS>();          // the direct loads of step 0
+        } else {
+            load_raw(0, raw[1]);
+            issue_dma(0, A0, B0);
+            load_raw(1, raw[0]);
+            issue_dma(1, A1, B1);
+            tied_wait(std::integral_constant<int, NXL + 2 * LPS>{}, raw[1]);
+            nrm_store(0, A0, raw[1]);
+            issue_fence(x, gamma, beta);
+            load_raw(2, raw[1]);
+            wait_vmcnt<2 * NXL + LPS>();      // the direct loads of step 0
+        }
     } else {
-        issue(0, A0, B0);
-        issue(1, A1, B1);
+        issue_dma(0, A0, B0);
+        issue_dma(1, A1, B1);
+        wait_vmcnt<LPS>();
     }
     issue_fence(x, gamma, beta);
-    wait_vmcnt<LPS>();                 // this wave's loads of step 0 have landed
-    issue_fence(x, gamma, beta);
-    if (k_tail && nk == 1) {
+    if (KT && nk == 1) {
         if constexpr (!AFFINE)
             zero_tail_x(A0);
         fix_tail(B0);
     }
     lds_barrier();
+    if (wm == 1) {
+        // the second group starts one phase later; its first phase does what
+        // each of its compute phases does for kt + 3 and kt + 2: the direct
+        // loads of step 2, and its x rows of step 1
+        issue_dma(2, A2, B2);
+        if constexpr (AFFINE) {
+            tied_wait(CX{}, raw[0]);
+            nrm_store(1, A1, raw[0]);
+            lds_barrier();
+        } else {
+            phase_barrier();
+        }
+    }
 
     floatx16 acc[FN][FM];
 #pragma unroll
@@ -526,168 +614,132 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[j][i][e] = 0.0f;
 
-    // Operand chunks of this lane for sub-step kk: rows 32 apart share the
-    // swizzle, so one offset per sub-step (plus compile-time row and stage
-    // offsets) addresses every fragment of every stage.
-    struct Frag {
-        u32x4 w[FN], a[FM];
+    // this wave's fragments of one K step: [sub-step][32-row block]; rows
+    // 32 apart share the swizzle, so one offset per sub-step addresses every
+    // fragment of a stage
+    u32x4 fa[4][FM], fb[4][FN];
+    auto read_frags = [&](const u32x4 *Ac, const u32x4 *Bc) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int sw = swz(lrow, kk * 2 + lk);
+            const int aoff = (wm * WM + lrow) * CPR + sw;
+            const int boff = (wn * WN + lrow) * CPR + sw;
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                fb[kk][j] = Bc[boff + j * 32 * CPR];
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+                fa[kk][i] = Ac[aoff + i * 32 * CPR];
+        }
     };
-    auto rdfrag = [&](const u32x4 *Ac, const u32x4 *Bc, int kk, Frag &f) {
-        const int sw = swz(lrow, kk * 2 + lk);
-        const int aoff = (wm * WM + lrow) * CPR + sw;
-        const int boff = (wn * WN + lrow) * CPR + sw;
+    auto mfma_kk = [&](int kk) {
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-            f.w[j] = Bc[boff + j * 32 * CPR];
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
-            f.a[i] = Ac[aoff + i * 32 * CPR];
+            for (int i = 0; i < FM; ++i)
+                acc[j][i] = mfma32<DT>(fb[kk][j], fa[kk][i], acc[j][i]);
     };
-    auto mm = [&](const Frag &f, int j) {
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-            acc[j][i] = mfma32<DT>(f.w[j], f.a[i], acc[j][i]);
-    };
-    auto sb = [] { __builtin_amdgcn_sched_barrier(0); };
-
-    // One K step on stage kt % 3. The direct loads of step kt + 2 go into the
-    // stage read in step kt - 1 (free since that step's barrier), one after
-    // a pair of MFMAs, so that the load unit is fed while the matrix cores
-    // run; fragments of the next sub-step are read before the MFMAs of the
-    // current one.
-    //   normalized x: the x / gamma / beta chunks of step kt + 1 are loaded
-    //   into registers at the start of the step; in sub-step 3 (younger are
-    //   only the three W loads issued since) they are normalized and written
-    //   once into stage (kt + 1) % 3, last read in step kt - 2. W goes one
-    //   load per sub-step.
-    //   plain x: x and W of step kt + 2 both go direct, in the first six
-    //   slots.
-    // At the end this wave's loads of step kt + 1 have landed (the LPS of
-    // step kt + 2 are the only younger ones); the barrier makes step kt + 1
-    // complete for every wave and frees stage kt % 3.
-    auto step = [&](int kt, auto sc) {
-        constexpr int s = decltype(sc)::value;
-        using S1 = std::integral_constant<int, s + 1>;
-        using S2 = std::integral_constant<int, s + 2>;
-        const u32x4 *Ac = Ast(sc);
-        const u32x4 *Bc = Bst(sc);
-        u32x4 *An = Ast(S2{}), *Bn = Bst(S2{});
-        const int kn = min(kt + 2, nk - 1);
-        const bool tl = KT && kn == nk - 1;
-        const char *wb = reinterpret_cast<const char *>(wtile) + (size_t)kn * (BK * 2);
-        const char *xb = reinterpret_cast<const char *>(xtile) + (size_t)kn * (BK * 2);
-        // load slot d: x chunks first when x goes direct, then W
-        auto slot = [&](auto dc) {
-            constexpr int d = decltype(dc)::value;
-            constexpr int NA = AFFINE ? 0 : A_DMA;
-            if constexpr (d < NA) {
-                dma16(xb, tl ? aoff_t[d] : aoff_g[d],
-                      lds_addr(&An[(d * A_IST + wave * 8) * CPR]));
-            } else if constexpr (d < LPS) {
-                constexpr int i = d - NA;
-                dma16(wb, tl ? woff_t[i] : woff[i],
-                      lds_addr(&Bn[(wave * B_RPW + i * 8) * CPR]));
-            }
-            sb();
-        };
-        using D0 = std::integral_constant<int, 0>;
-        using D1 = std::integral_constant<int, 1>;
-        using D2 = std::integral_constant<int, 2>;
-        using D3 = std::integral_constant<int, 3>;
-        using D4 = std::integral_constant<int, 4>;
-        using D5 = std::integral_constant<int, 5>;
-        Frag f0, f1;
-        issue_fence(x, gamma, beta);
+    // the step's MFMAs; with normalization, x of step kn from buffer r is
+    // normalized into stage As between them (chunk 0 after sub-step 0,
+    // chunk 1 after sub-step 1), so the VALU work issues while the matrix
+    // core runs this wave's MFMAs
+    auto compute = [&](int kn, u32x4 *As, NormRaw &r) {
+        mfma_kk(0);
+        sb();
         if constexpr (AFFINE) {
-            static_assert(LPS == 4, "one W load per sub-step");
-            issue_gb(kt + 2, Gst(S2{}));
-            NormRaw raw;
-            load_raw(kt + 1, raw);
-            // published by the barrier that ended step kt - 1
-            read_gb(Gst(S1{}), raw);
+            nrm_chunk(kn, As, r, 0);
             sb();
-            rdfrag(Ac, Bc, 0, f0);
+            mfma_kk(1);
             sb();
-            rdfrag(Ac, Bc, 1, f1);
-            sb();
-            mm(f0, 0);
-            sb();
-            slot(D0{});
-            mm(f0, 1);
-            sb();
-            rdfrag(Ac, Bc, 2, f0);
-            sb();
-            mm(f1, 0);
-            sb();
-            slot(D1{});
-            mm(f1, 1);
-            sb();
-            rdfrag(Ac, Bc, 3, f1);
-            sb();
-            mm(f0, 0);
-            sb();
-            slot(D2{});
-            mm(f0, 1);
-            sb();
-            wait_vmcnt_tied<3>(raw.v[0], raw.v[1], raw.g, raw.b);
-            mm(f1, 0);
-            // (in the last step this normalizes a stage that is never read)
-            nrm_store(kt + 1, Ast(S1{}), raw);
-            sb();
-            slot(D3{});
-            mm(f1, 1);
+            nrm_chunk(kn, As, r, 1);
             sb();
         } else {
-            static_assert(LPS == 6, "six direct loads per K step");
-            rdfrag(Ac, Bc, 0, f0);
-            sb();
-            rdfrag(Ac, Bc, 1, f1);
-            sb();
-            mm(f0, 0);
-            sb();
-            slot(D0{});
-            mm(f0, 1);
-            sb();
-            slot(D1{});
-            rdfrag(Ac, Bc, 2, f0);
-            sb();
-            mm(f1, 0);
-            sb();
-            slot(D2{});
-            mm(f1, 1);
-            sb();
-            slot(D3{});
-            rdfrag(Ac, Bc, 3, f1);
-            sb();
-            mm(f0, 0);
-            sb();
-            slot(D4{});
-            mm(f0, 1);
-            sb();
-            slot(D5{});
-            mm(f1, 0);
-            sb();
-            mm(f1, 1);
+            mfma_kk(1);
             sb();
         }
-        wait_vmcnt<LPS>();
-        issue_fence(x, gamma, beta);
-        if (k_tail && kt + 1 == nk - 1) {
+        mfma_kk(2);
+        sb();
+        mfma_kk(3);
+        sb();
+    };
+    auto tail_fix = [&](int kt, auto s1) {
+        if (KT && kt + 1 == nk - 1) {
             if constexpr (!AFFINE)
-                zero_tail_x(Ast(S1{}));
-            fix_tail(Bst(S1{}));
+                zero_tail_x(Ast(s1));
+            fix_tail(Bst(s1));
+        }
+    };
+
+    // one K step (memory phase, then compute phase) of this wave; J = kt % 6
+    // gives the stages (J % 3, + 1, + 2) and the x buffers. The MFMAs are one
+    // code path for both groups (so the accumulators stay in place); the
+    // groups differ only in which loads they issue and await where, and in
+    // the step they normalize (group 0: kt + 1, group 1: kt + 2).
+    auto kstep = [&](int kt, auto jc) {
+        constexpr int J = decltype(jc)::value;
+        using S0 = std::integral_constant<int, J % 3>;
+        using S1 = std::integral_constant<int, J % 3 + 1>;
+        using S2 = std::integral_constant<int, J % 3 + 2>;
+        NormRaw &rl = raw[J % 2];           // loaded in this memory phase
+        NormRaw &rn = raw[(J + 1) % 2];     // normalized in this compute phase
+        issue_fence(x, gamma, beta);
+        // memory phase
+        read_frags(Ast(S0{}), Bst(S0{}));
+        sb();
+        if constexpr (AFFINE)
+            load_raw(kt + 2 + wm, rl);
+        if (wm == 0) {
+            issue_dma(kt + 2, Ast(S2{}), Bst(S2{}));
+        } else {
+            wait_vmcnt<AFFINE ? CW : LPS>();   // the direct loads of kt + 1
+            issue_fence(x, gamma, beta);
+            tail_fix(kt, S1{});
+        }
+        lds_barrier();
+        // compute phase
+        sb();
+        if (wm == 1)
+            issue_dma(kt + 3, Ast(S0{}), Bst(S0{}));
+        if constexpr (AFFINE)
+            tied_wait(CX{}, rn);
+        sb();
+        compute(kt + 1 + wm, wm ? Ast(S2{}) : Ast(S1{}), rn);
+        if (wm == 0) {
+            wait_vmcnt<AFFINE ? CL : LPS>();   // the direct loads of kt + 1
+            issue_fence(x, gamma, beta);
+            tail_fix(kt, S1{});
         }
         lds_barrier();
     };
-    for (int kt = 0; kt < nk; kt += NSTAGE) {
-        step(kt, I0{});
+    using J0 = std::integral_constant<int, 0>;
+    using J1 = std::integral_constant<int, 1>;
+    using J2 = std::integral_constant<int, 2>;
+    using J3 = std::integral_constant<int, 3>;
+    using J4 = std::integral_constant<int, 4>;
+    using J5 = std::integral_constant<int, 5>;
+    for (int kt = 0; kt < nk; kt += 6) {
+        kstep(kt, J0{});
         if (kt + 1 < nk)
-            step(kt + 1, I1{});
+            kstep(kt + 1, J1{});
         if (kt + 2 < nk)
-            step(kt + 2, I2{});
+            kstep(kt + 2, J2{});
+        if (kt + 3 < nk)
+            kstep(kt + 3, J3{});
+        if (kt + 4 < nk)
+            kstep(kt + 4, J4{});
+        if (kt + 5 < nk)
+            kstep(kt + 5, J5{});
     }
-    // drain the clamped loads issued past the last step before LDS reuse
-    wait_vmcnt<0>();
+    if (wm == 0)
+        phase_barrier();        // the second group's last compute phase
+    // drain the clamped loads issued past the last step before LDS reuse; the
+    // x registers of the last (unused) loads stay live until they have landed
+    if constexpr (AFFINE) {
+        tied_wait(C0{}, raw[0]);
+        tied_wait(C0{}, raw[1]);
+    } else {
+        wait_vmcnt<0>();
+    }
     __syncthreads();
 
     if constexpr (SK) {
@@ -740,8 +792,8 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
                 float v[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    v[r] = apply_act(acc[0][i][q * 4 + r] + bg[r], act) *
-                           (acc[1][i][q * 4 + r] + bu[r]);
+                    v[r] = apply_act(fmaf(acc[0][i][q * 4 + r], osc[i], bg[r]), act) *
+                           fmaf(acc[1][i][q * 4 + r], osc[i], bu[r]);
                 const int chunk = (nl >> 3) ^ (ml & 15);
                 uint32_t *dst = reinterpret_cast<uint32_t *>(&B0[ml * 16 + chunk]) + (lk * 2);
                 dst[0] = pack2<DT>(v[0], v[1]);
@@ -789,7 +841,7 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
                     float v[4];
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        v[r] = apply_act(acc[j][i][q * 4 + r] + bv[r], act);
+                        v[r] = apply_act(fmaf(acc[j][i][q * 4 + r], osc[i], bv[r]), act);
                     const int chunk = (nl >> 3) ^ (ml & 31);
                     uint32_t *dst = reinterpret_cast<uint32_t *>(&stg[ml * 32 + chunk]) + (lk * 2);
                     dst[0] = pack2<DT>(v[0], v[1]);
@@ -820,7 +872,7 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
     }
 }
 
-template <int DT, int STATS, int GB, bool KT, bool LN, bool GT, bool SK = false>
+template <int DT, int STATS, int GB, bool KT, bool GT, bool SK = false>
 hipError_t launch_k(const GemmArgs &a, hipStream_t s, float *part = nullptr, int ksplit = 1)
 {
     const int cus = cu_count();
@@ -831,7 +883,7 @@ hipError_t launch_k(const GemmArgs &a, hipStream_t s, float *part = nullptr, int
     mp.T = mp.tm * mp.tn;
     mp.xcd = (cus % 8 == 0 && mp.tn % 8 == 0) ? 1 : 0;
     const int vec_out = (a.N % 8 == 0 && ((uintptr_t)a.y & 15u) == 0) ? 1 : 0;
-    if constexpr (STATS == ST_FROM_Y) {
+    if constexpr (STATS == ST_FROM_Y || STATS == ST_FROM_Y_PS) {
         hipLaunchKernelGGL((row_stats_to_y_kernel<DT>), dim3((unsigned)((a.M + 3) / 4)), dim3(256),
                            0, s, (const uint16_t *)a.x, (uint16_t *)a.y, (int)a.M, (int)a.N,
                            (int)a.K, a.eps, a.norm, mp.tn, BNO);
@@ -839,7 +891,7 @@ hipError_t launch_k(const GemmArgs &a, hipStream_t s, float *part = nullptr, int
         if (e != hipSuccess)
             return e;
     }
-    hipLaunchKernelGGL((prefill_lds_kernel<DT, STATS, GB, KT, LN, GT, SK>), dim3(mp.T * ksplit),
+    hipLaunchKernelGGL((prefill_lds_kernel<DT, STATS, GB, KT, GT, SK>), dim3(mp.T * ksplit),
                        dim3(THREADS), 0, s,
                        (const uint16_t *)a.x, (const uint16_t *)a.gamma, (const uint16_t *)a.beta,
                        (const uint16_t *)a.W, (const uint16_t *)a.bias, (uint16_t *)a.y, (int)a.M,
@@ -847,41 +899,42 @@ hipError_t launch_k(const GemmArgs &a, hipStream_t s, float *part = nullptr, int
     return hipGetLastError();
 }
 
-template <int DT, int STATS, int GB, bool LN, bool GT>
+template <int DT, int STATS, int GB, bool GT>
 hipError_t launch_t(const GemmArgs &a, hipStream_t s)
 {
-    return a.K % BK ? launch_k<DT, STATS, GB, true, LN, GT>(a, s)
-                    : launch_k<DT, STATS, GB, false, LN, GT>(a, s);
-}
-
-template <int DT, int STATS, bool LN, bool GT>
-hipError_t launch_gb(const GemmArgs &a, hipStream_t s)
-{
-    switch ((a.gamma ? 1 : 0) | (a.beta ? 2 : 0)) {
-    case 0: return launch_t<DT, STATS, 0, LN, GT>(a, s);
-    case 1: return launch_t<DT, STATS, 1, LN, GT>(a, s);
-    case 2: return launch_t<DT, STATS, 2, LN, GT>(a, s);
-    default: return launch_t<DT, STATS, 3, LN, GT>(a, s);
-    }
+    return a.K % BK ? launch_k<DT, STATS, GB, true, GT>(a, s)
+                    : launch_k<DT, STATS, GB, false, GT>(a, s);
 }
 
 template <int DT, int STATS, bool GT>
 hipError_t launch_norm(const GemmArgs &a, hipStream_t s)
 {
-    return a.norm == NORM_LAYERNORM ? launch_gb<DT, STATS, true, GT>(a, s)
-                                    : launch_gb<DT, STATS, false, GT>(a, s);
+    switch ((a.gamma ? 1 : 0) | (a.beta ? 2 : 0)) {
+    case 0: return launch_t<DT, STATS, 0, GT>(a, s);
+    case 1: return launch_t<DT, STATS, 1, GT>(a, s);
+    case 2: return launch_t<DT, STATS, 2, GT>(a, s);
+    default: return launch_t<DT, STATS, 3, GT>(a, s);
+    }
 }
 
 template <int DT, bool GT>
 hipError_t launch_dt(const GemmArgs &a, hipStream_t s)
 {
     if (a.norm == NORM_NONE)
-        return launch_t<DT, ST_NONE, 0, false, GT>(a, s);
+        return launch_t<DT, ST_NONE, 0, GT>(a, s);
     // The statistics pass needs 8 bytes of y in every tile's rows: every
     // tile (including the last, partial one) must have at least 4 columns
     // and the rows must be 8-byte aligned.
     const bool y_scratch = a.N % 8 == 0 && ((uintptr_t)a.y & 15u) == 0;
-    return y_scratch ? launch_norm<DT, ST_FROM_Y, GT>(a, s) : launch_norm<DT, ST_PROLOGUE, GT>(a, s);
+    if (!y_scratch)
+        return launch_norm<DT, ST_PROLOGUE, GT>(a, s);
+    // fp16 RMSNorm without beta: power-of-two prescaled operand
+    if constexpr (DT == DT_F16) {
+        if (a.norm == NORM_RMSNORM && !a.beta)
+            return a.gamma ? launch_t<DT, ST_FROM_Y_PS, 1, GT>(a, s)
+                           : launch_t<DT, ST_FROM_Y_PS, 0, GT>(a, s);
+    }
+    return launch_norm<DT, ST_FROM_Y, GT>(a, s);
 }
 
 }  // namespace
@@ -914,10 +967,10 @@ hipError_t launch_prefill_lds_splitk(const GemmArgs &a, float *part, int ksplit,
         return hipErrorInvalidValue;
     const bool kt = a.K % BK != 0;
     if (a.dtype == DT_F16)
-        return kt ? launch_k<DT_F16, ST_NONE, 0, true, false, false, true>(a, s, part, ksplit)
-                  : launch_k<DT_F16, ST_NONE, 0, false, false, false, true>(a, s, part, ksplit);
-    return kt ? launch_k<DT_BF16, ST_NONE, 0, true, false, false, true>(a, s, part, ksplit)
-              : launch_k<DT_BF16, ST_NONE, 0, false, false, false, true>(a, s, part, ksplit);
+        return kt ? launch_k<DT_F16, ST_NONE, 0, true, false, true>(a, s, part, ksplit)
+                  : launch_k<DT_F16, ST_NONE, 0, false, false, true>(a, s, part, ksplit);
+    return kt ? launch_k<DT_BF16, ST_NONE, 0, true, false, true>(a, s, part, ksplit)
+              : launch_k<DT_BF16, ST_NONE, 0, false, false, true>(a, s, part, ksplit);
 }
 
 hipError_t launch_prefill_lds_gated(const GemmArgs &a, hipStream_t s)

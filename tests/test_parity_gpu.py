@@ -538,6 +538,30 @@ def test_fp16_layernorm_extreme_rows_eps0(M, K):
     check_full(case)
 
 
+@pytest.mark.parametrize("M,K,gamma,eps", [(96, 512, True, 0.0), (150, 2056, False, 0.0),
+                                            (40, 264, True, 1e-6), (300, 1024, True, 1e-5)])
+def test_fp16_rmsnorm_prescale_extreme_rows(M, K, gamma, eps):
+    """fp16 RMSNorm without beta on the tiled kernel scales each row by a
+    power of two 2^e <= 1/rms before the single fp16 rounding, with e clamped
+    to -14..15, and rescales the fp32 sum by rs 2^-e: rows whose 1/rms is ~1e7
+    (clamped at 2^15), rows of +-40000 (clamped at 2^-14) and ordinary rows
+    must all match the oracle."""
+    case = synth.make_norm_gemm(f"rms_prescale_{M}x{K}_g{gamma}", M, K, 72, norm=RMS, act=SILU,
+                                gamma=gamma, beta=False, eps=eps, seed=M + K)
+    case.arrays["x"] = _extreme_rows(M, K, seed=M + 1)
+    check_full(case)
+
+
+@pytest.mark.parametrize("M", [40, 130])
+def test_gated_ffn_rmsnorm_prescale(M):
+    """The gated tiles take the same prescaled operand and rescale both the
+    gate and the up sums of a row before act(gate) * up."""
+    case = synth.make_gated_ffn(f"gated_prescale_{M}", M, 264, 384, 136, norm=RMS, act=SILU,
+                                gamma=True, beta=False, b1=True, b2=True, eps=1e-6, seed=M)
+    case.arrays["x"] = _extreme_rows(M, 264, seed=M + 2)
+    check_full(case)
+
+
 @pytest.mark.parametrize("M", [24, 200])
 def test_large_mean_layernorm_k14336_tight(M):
     """x ~ N(4, 1) at K = 14336 with gamma and beta: the fp32 normalization is
