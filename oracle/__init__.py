@@ -75,6 +75,13 @@ def lib():
         L.oracle_ffn.restype = ctypes.c_int
         L.oracle_gated_ffn.argtypes = L.oracle_ffn.argtypes
         L.oracle_gated_ffn.restype = ctypes.c_int
+        L.oracle_fold_weights.argtypes = [p16, p16, p16, p16, i64, i64, ctypes.c_int, pf64,
+                                          pf64, pf64]
+        L.oracle_fold_weights.restype = ctypes.c_int
+        L.oracle_norm_gemm_folded.argtypes = [p16, pf64, pf64, pf64, i64, i64, i64,
+                                              ctypes.c_float, ctypes.c_int, ctypes.c_int,
+                                              ctypes.c_int, pi64, i64, pi64, i64, pf64]
+        L.oracle_norm_gemm_folded.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -185,3 +192,50 @@ def run_case(case, rows=None, cols=None) -> np.ndarray:
                    rows, cols, gated=case.kind == "gated_ffn")
     return norm_gemm(A["x"], A.get("gamma"), A.get("beta"), A["W"], A.get("bias"),
                      case.eps, case.norm, case.act, case.dtype, rows, cols)
+
+
+def _f64(a: Optional[np.ndarray]):
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    return a, a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def fold_weights(W, gamma, beta, bias, dtype: int, want_w: bool = True):
+    """Folded weights of the inference-mode strategy: (W' = W * gamma [N,K]
+    fp64 or None, c1 = W' 1 [N], c2 = W beta + bias [N])."""
+    N, K = W.shape
+    w, pw = _u16(W)
+    g, pg = _u16(gamma)
+    b, pb = _u16(beta)
+    bi, pbi = _u16(bias)
+    Wf = np.empty((N, K), dtype=np.float64) if want_w else None
+    c1 = np.empty(N, dtype=np.float64)
+    c2 = np.empty(N, dtype=np.float64)
+    pf = None if Wf is None else Wf.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+    rc = lib().oracle_fold_weights(pw, pg, pb, pbi, N, K, dtype, pf,
+                                   c1.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+                                   c2.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
+    if rc != 0:
+        raise ValueError(f"oracle_fold_weights failed ({rc})")
+    return Wf, c1, c2
+
+
+def norm_gemm_folded(x, Wf, c1, c2, eps: float, norm: int, act: int, dtype: int,
+                     rows: Optional[Sequence[int]] = None,
+                     cols: Optional[Sequence[int]] = None) -> np.ndarray:
+    """y = act(r (x Wf^T - mu c1) + c2) with the definition's row statistics."""
+    M, K = x.shape
+    N = Wf.shape[0]
+    assert Wf.shape[1] == K and c1.shape == (N,) and c2.shape == (N,)
+    x, px = _u16(x)
+    wf, pwf = _f64(Wf)
+    a1, p1 = _f64(c1)
+    a2, p2 = _f64(c2)
+    r, pr = _idx(rows, M)
+    c, pc = _idx(cols, N)
+    out = np.empty((len(r), len(c)), dtype=np.float64)
+    rc = lib().oracle_norm_gemm_folded(px, pwf, p1, p2, M, N, K, eps, norm, act, dtype,
+                                       pr, len(r), pc, len(c),
+                                       out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
+    if rc != 0:
+        raise ValueError(f"oracle_norm_gemm_folded failed ({rc})")
+    return out

@@ -317,3 +317,93 @@ int oracle_gated_ffn(const uint16_t *x, const uint16_t *gamma, const uint16_t *b
     return ffn_impl(x, gamma, beta, W1, b1, W2, b2, M, K, F, N, eps, norm, act, dtype, 1, rows,
                     n_rows, cols, n_cols, y_out);
 }
+
+/* Inference-mode folding (page "LayerNorm 融合算子如何让大模型推理再快 15%？深度拆解
+ * ATB 的实现", section 6.2, tip 2: in inference gamma and beta are fixed, so
+ * gamma is folded once, ahead of time, into the weights of the MatMul that
+ * follows, which saves the multiplication after the normalization). The
+ * algebra of the unfused definition, with xhat = (x - mu) r (RMSNorm: mu = 0):
+ *   z_n = sum_k (xhat_k gamma_k + beta_k) W[n,k] + bias_n
+ *       = r (sum_k x_k W'[n,k] - mu c1_n) + c2_n
+ *   W'[n,k] = W[n,k] gamma_k,  c1_n = sum_k W'[n,k],
+ *   c2_n = sum_k W[n,k] beta_k + bias_n.
+ * oracle_fold_weights computes W' (fp64, exact: a product of two 16-bit
+ * values), c1 and c2; gamma == NULL means 1, beta or bias == NULL means 0.
+ * Wf may be NULL (only c1, c2). */
+int oracle_fold_weights(const uint16_t *W, const uint16_t *gamma, const uint16_t *beta,
+                        const uint16_t *bias, int64_t N, int64_t K, int dtype, double *Wf,
+                        double *c1, double *c2)
+{
+    if (N < 1 || K < 1 || !W || !c1 || !c2 || (dtype != OR_F16 && dtype != OR_BF16))
+        return OR_ERR_ARG;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t n = 0; n < N; ++n) {
+        double s1 = 0.0, s2 = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double w = dec(W[n * K + k], dtype);
+            double g = gamma ? dec(gamma[k], dtype) : 1.0;
+            double b = beta ? dec(beta[k], dtype) : 0.0;
+            double wf = w * g;
+            if (Wf)
+                Wf[n * K + k] = wf;
+            s1 += wf;
+            s2 += w * b;
+        }
+        c1[n] = s1;
+        c2[n] = s2 + (bias ? dec(bias[n], dtype) : 0.0);
+    }
+    return OR_OK;
+}
+
+/* y[i, j] = act( r (sum_k x[rows[i], k] Wf[cols[j], k] - mu c1[cols[j]]) + c2[cols[j]] )
+ * with the row statistics of the definition (LayerNorm: mean and biased
+ * variance, two passes; RMSNorm: mu = 0, r = 1/sqrt(mean(x^2) + eps)), for
+ * given folded weights Wf [N,K] and vectors c1, c2 (fp64). With the outputs of
+ * oracle_fold_weights it equals oracle_norm_gemm up to fp64 rounding. */
+int oracle_norm_gemm_folded(const uint16_t *x, const double *Wf, const double *c1,
+                            const double *c2, int64_t M, int64_t N, int64_t K, float eps,
+                            int norm, int act, int dtype, const int64_t *rows, int64_t n_rows,
+                            const int64_t *cols, int64_t n_cols, double *y_out)
+{
+    if (check_common(M, K, norm, act, dtype) || N < 1 || norm == OR_NORM_NONE || !x || !Wf ||
+        !c1 || !c2 || !rows || !cols || !y_out)
+        return OR_ERR_ARG;
+    for (int64_t i = 0; i < n_rows; ++i)
+        if (rows[i] < 0 || rows[i] >= M)
+            return OR_ERR_ARG;
+    for (int64_t j = 0; j < n_cols; ++j)
+        if (cols[j] < 0 || cols[j] >= N)
+            return OR_ERR_ARG;
+    const double e = (double)eps;
+    int64_t total = n_rows * n_cols;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t t = 0; t < total; ++t) {
+        int64_t i = t / n_cols, j = t % n_cols;
+        const uint16_t *xr = x + rows[i] * K;
+        double mu = 0.0, r;
+        if (norm == OR_NORM_LAYERNORM) {
+            double s = 0.0, q = 0.0;
+            for (int64_t k = 0; k < K; ++k)
+                s += dec(xr[k], dtype);
+            mu = s / (double)K;
+            for (int64_t k = 0; k < K; ++k) {
+                double d = dec(xr[k], dtype) - mu;
+                q += d * d;
+            }
+            r = 1.0 / sqrt(q / (double)K + e);
+        } else {
+            double q = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double v = dec(xr[k], dtype);
+                q += v * v;
+            }
+            r = 1.0 / sqrt(q / (double)K + e);
+        }
+        const double *wr = Wf + cols[j] * K;
+        double acc = 0.0;
+        for (int64_t k = 0; k < K; ++k)
+            acc += dec(xr[k], dtype) * wr[k];
+        y_out[t] = apply_act(r * (acc - mu * c1[cols[j]]) + c2[cols[j]], act);
+    }
+    return OR_OK;
+}

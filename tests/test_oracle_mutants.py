@@ -39,6 +39,18 @@ MUTATIONS = {
                       "v = ldexp(1.0 + (double)f / 256.0, e - 127);"),
 }
 
+# Mistakes in the inference-mode folding, caught by its own pins.
+FOLD_MUTATIONS = {
+    "fold_c1_sign": ("y_out[t] = apply_act(r * (acc - mu * c1[cols[j]]) + c2[cols[j]], act);",
+                     "y_out[t] = apply_act(r * (acc + mu * c1[cols[j]]) + c2[cols[j]], act);"),
+    "fold_c2_without_bias": ("c2[n] = s2 + (bias ? dec(bias[n], dtype) : 0.0);", "c2[n] = s2;"),
+    "fold_gamma_dropped": ("double wf = w * g;", "double wf = w;"),
+    "fold_c1_of_unfolded_w": ("s1 += wf;", "s1 += w;"),
+}
+PIN_FILE = {name: "test_oracle_pins.py" for name in MUTATIONS}
+PIN_FILE.update({name: "test_oracle_fold.py" for name in FOLD_MUTATIONS})
+MUTATIONS.update(FOLD_MUTATIONS)
+
 
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
 def test_pins_catch_planted_mistake(name, tmp_path):
@@ -52,6 +64,6 @@ def test_pins_catch_planted_mistake(name, tmp_path):
                     str(lib), str(mutated), "-lm"], check=True)
     env = dict(os.environ, NORM_GEMM_ORACLE_LIB=str(lib), OMP_NUM_THREADS="2")
     res = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
-                          os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                          os.path.join(ROOT, "tests", PIN_FILE[name])],
                          cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert res.returncode != 0, f"pins did not catch mutation {name}:\n{res.stdout[-2000:]}"
