@@ -46,8 +46,11 @@ PEAK_MFMA_F16_TFLOPS = 2516.6   # 256 CUs x 2.4 GHz x 4096 dense fp16/bf16 FLOP/
 PEAK_HBM_GBS = 8000.0           # HBM3E, 8 TB/s
 LLC_BYTES = 256 << 20           # Infinity Cache (MALL)
 HEADLINE = "rms_matmul_silu_512x14336"
+# ":folded" = the same workload with gamma / beta folded into the weights
+# (inference mode), the folding itself done once before the timed region
 EXTRAS = ("ffn_silu_512x14336x49152", "ln_linear_bias_1024x8192", "decode_rms_gemm_m1",
-          "decode_rms_gemm_m8", "decode_rms_gemm_m32", "ln_linear_bias_64x256")
+          "decode_rms_gemm_m8", "decode_rms_gemm_m32", "ln_linear_bias_64x256",
+          "rms_matmul_silu_512x14336:folded", "ln_linear_bias_1024x8192:folded")
 
 
 def workload(name: str):
@@ -117,7 +120,9 @@ def measure(name: str, steps: int, warmup: int):
     import torch
     import norm_gemm_amd as ng
 
-    case = workload(name)
+    base_name, _, mode = name.partition(":")
+    folded = mode == "folded"
+    case = workload(base_name)
     dev = torch.device("cuda:0")
     A = case.arrays
     flops, nbytes = algorithmic(case)
@@ -131,6 +136,11 @@ def measure(name: str, steps: int, warmup: int):
     up = {k: upload(v, case.dtype, dev) for k, v in A.items() if v is not None and k not in wkeys}
     base = {k: upload(A[k], case.dtype, dev) for k in wkeys}
     wsets = [{k: (base[k] if c == 0 else base[k].clone()) for k in wkeys} for c in range(copies)]
+    if folded:
+        for w in wsets:
+            w["W"], w["c1"], w["c2"] = ng.norm_gemm_fold_weights(
+                w["W"], up.get("gamma"), up.get("beta"), up.get("bias"))
+        torch.cuda.synchronize()
     get = up.get
     out = torch.empty(case.M, case.N, dtype=up["x"].dtype, device=dev)
     ws = None
@@ -143,6 +153,9 @@ def measure(name: str, steps: int, warmup: int):
             ffn_call(get("x"), w["W1"], w["W2"], get("gamma"), get("beta"), get("b1"),
                      get("b2"), eps=case.eps, norm=case.norm, act=case.act,
                      workspace=ws, out=out)
+        elif folded:
+            ng.fused_norm_gemm_folded(get("x"), w["W"], w["c1"], w["c2"], eps=case.eps,
+                                      norm=case.norm, act=case.act, out=out)
         else:
             ng.fused_norm_gemm(get("x"), w["W"], get("gamma"), get("beta"), get("bias"),
                                eps=case.eps, norm=case.norm, act=case.act, out=out)
@@ -173,7 +186,7 @@ def measure(name: str, steps: int, warmup: int):
         value = flops / (ms_per_step * 1e-3) / 1e12
         unit, bound, peak, runit = "TFLOP/s", "mfma", PEAK_MFMA_F16_TFLOPS, "TFLOP/s"
     res = {
-        "workload": case.name,
+        "workload": case.name + (" (gamma/beta folded into the weights)" if folded else ""),
         "value": round(value, 2),
         "unit": unit,
         "ms_per_step": round(ms_per_step, 5),

@@ -60,8 +60,9 @@
 extern "C" {
 #endif
 
-#define NORM_GEMM_ABI_VERSION 4   /* 2: NG_ACT_RELU, NG_ACT_GELU; 3: fused_gated_ffn;
-                                     4: fused_ffn_noalloc, NG_ERR_SCRATCH */
+#define NORM_GEMM_ABI_VERSION 5   /* 2: NG_ACT_RELU, NG_ACT_GELU; 3: fused_gated_ffn;
+                                     4: fused_ffn_noalloc, NG_ERR_SCRATCH;
+                                     5: norm_gemm_fold_weights, fused_norm_gemm_folded */
 
 typedef enum { NG_NORM_NONE = 0, NG_NORM_LAYERNORM = 1, NG_NORM_RMSNORM = 2 } ng_norm_t;
 typedef enum { NG_ACT_NONE = 0, NG_ACT_SILU = 1, NG_ACT_RELU = 2, NG_ACT_GELU = 3 } ng_act_t;
@@ -153,6 +154,43 @@ int fused_gated_ffn(const void *x, const void *gamma, const void *beta,
                     void *y, int64_t M, int64_t K, int64_t F, int64_t N,
                     float eps, int norm, int act, int dtype,
                     void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Inference-mode folding (page "LayerNorm 融合算子如何让大模型推理再快 15%？深度拆解
+ * ATB 的实现", section 6.2, tip 2: at inference gamma and beta are fixed, so
+ * gamma is folded once, ahead of time, into the weights of the MatMul that
+ * follows). With xhat = (x - mu) rs the row normalized without its affine
+ * terms (RMSNorm: mu = 0),
+ *     y[m,n] = act( sum_k (xhat_k gamma_k + beta_k) W[n,k] + bias[n] )
+ *            = act( rs_m (sum_k x[m,k] W'[n,k] - mu_m c1[n]) + c2[n] )
+ *     W'[n,k] = W[n,k] gamma[k],  c1[n] = sum_k W'[n,k],
+ *     c2[n]   = sum_k W[n,k] beta[k] + bias[n].
+ *
+ * norm_gemm_fold_weights: prepares W_folded ([N,K], dtype, each element
+ * W[n,k] gamma[k] rounded once), c1 and c2 ([N] fp32; c1 sums the rounded
+ * W_folded so that the GEMM's sums centre exactly). gamma == NULL means 1;
+ * beta or bias == NULL means 0. All pointers are caller-owned device memory;
+ * W_folded, c1 and c2 must not overlap each other or an input (NG_ERR_ALIAS);
+ * c1 and c2 4-byte aligned. Reads W once, writes W_folded once, on `stream`.
+ *
+ * fused_norm_gemm_folded: y = act(rs (x . W_folded^T - mu c1) + c2) for
+ * norm = LayerNorm or RMSNorm (NG_ERR_ENUM otherwise) with the row statistics
+ * of fused_norm_gemm; x goes to the matrix cores unnormalized, and the
+ * statistics and c1, c2 are applied in the epilogue in fp32. c1 is required
+ * for LayerNorm and not read for RMSNorm; c2 is required. The GEMM runs on
+ * the tiled kernel for any M: x and W_folded must be 16-byte aligned with
+ * K % 8 == 0 and K <= 8,388,600, else NG_ERR_UNSUPPORTED. With |mean| >>
+ * sigma the difference x . W'^T - mu c1 cancels in fp32; fused_norm_gemm
+ * (which centres the row before the product) is the accurate choice there.
+ * Other conventions as fused_norm_gemm. Return an ng_status_t.
+ */
+int norm_gemm_fold_weights(const void *W, const void *gamma, const void *beta,
+                           const void *bias, void *W_folded, float *c1, float *c2,
+                           int64_t N, int64_t K, int dtype, void *stream);
+
+int fused_norm_gemm_folded(const void *x, const void *W_folded, const float *c1,
+                           const float *c2, void *y, int64_t M, int64_t N, int64_t K,
+                           float eps, int norm, int act, int dtype, void *stream);
 
 /*
  * fused_ffn_noalloc: fused_ffn for callers that cannot allocate device memory

@@ -7,6 +7,8 @@ supplies device memory and the stream. The functions mirror the C ABI in
 * :func:`fused_norm_gemm` -- y = act(norm_affine(x) @ W.T + bias)
 * :func:`fused_ffn` -- y = act(norm_affine(x) @ W1.T + b1) @ W2.T + b2
 * :func:`fused_ffn_noalloc` -- the FFN with the library's static workspace
+* :func:`norm_gemm_fold_weights`, :func:`fused_norm_gemm_folded` --
+  inference-mode folding of gamma / beta into the weights
 * :func:`fused_ffn_workspace_size`, :func:`norm_gemm_status_string`,
   :func:`norm_gemm_abi_version`
 
@@ -32,8 +34,8 @@ DTYPES = {torch.float16: 0, torch.bfloat16: 1}
 
 # Symbols declared in include/norm_gemm.h.
 EXPORTED = ("fused_norm_gemm", "fused_ffn", "fused_ffn_workspace_size", "fused_gated_ffn",
-            "fused_gated_ffn_workspace_size", "fused_ffn_noalloc", "norm_gemm_status_string",
-            "norm_gemm_abi_version")
+            "fused_gated_ffn_workspace_size", "fused_ffn_noalloc", "norm_gemm_fold_weights",
+            "fused_norm_gemm_folded", "norm_gemm_status_string", "norm_gemm_abi_version")
 
 # Size of the static device array behind fused_ffn_noalloc
 # (NG_FFN_NOALLOC_SCRATCH_BYTES in include/norm_gemm.h).
@@ -65,6 +67,10 @@ def _load() -> ctypes.CDLL:
     L.fused_ffn_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, f32, ci,
                                     ci, ci, vp]
     L.fused_ffn_noalloc.restype = ci
+    L.norm_gemm_fold_weights.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, ci, vp]
+    L.norm_gemm_fold_weights.restype = ci
+    L.fused_norm_gemm_folded.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, f32, ci, ci, ci, vp]
+    L.fused_norm_gemm_folded.restype = ci
     L.norm_gemm_status_string.argtypes = [ci]
     L.norm_gemm_status_string.restype = ctypes.c_char_p
     L.norm_gemm_abi_version.argtypes = []
@@ -246,4 +252,65 @@ def _ffn(gated, x, w1, w2, gamma, beta, b1, b2, eps, norm, act, workspace, out, 
             st = fn(*common, _ptr(workspace), ws_bytes, _stream(dev, stream))
     if st != 0:
         raise NormGemmError(st, what)
+    return out
+
+
+def norm_gemm_fold_weights(weight: torch.Tensor, gamma: Optional[torch.Tensor] = None,
+                           beta: Optional[torch.Tensor] = None,
+                           bias: Optional[torch.Tensor] = None, *, stream=None):
+    """Folded weights for :func:`fused_norm_gemm_folded`: returns (w_folded
+    [N, K] = weight * gamma rounded once, c1 = w_folded.sum(1) in fp32,
+    c2 = weight @ beta + bias in fp32)."""
+    if not isinstance(weight, torch.Tensor) or weight.dim() != 2:
+        raise ValueError("weight must be a [N, K] tensor")
+    if weight.dtype not in DTYPES:
+        raise ValueError(f"weight must be float16 or bfloat16, got {weight.dtype}")
+    dev = weight.device
+    N, K = weight.shape
+    _check(weight, "weight", weight.dtype, dev)
+    _check(gamma, "gamma", weight.dtype, dev, (K,))
+    _check(beta, "beta", weight.dtype, dev, (K,))
+    _check(bias, "bias", weight.dtype, dev, (N,))
+    wf = torch.empty_like(weight)
+    c1 = torch.empty(N, dtype=torch.float32, device=dev)
+    c2 = torch.empty(N, dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        st = lib.norm_gemm_fold_weights(_ptr(weight), _ptr(gamma), _ptr(beta), _ptr(bias),
+                                        _ptr(wf), _ptr(c1), _ptr(c2), N, K,
+                                        DTYPES[weight.dtype], _stream(dev, stream))
+    if st != 0:
+        raise NormGemmError(st, "norm_gemm_fold_weights")
+    return wf, c1, c2
+
+
+def fused_norm_gemm_folded(x: torch.Tensor, w_folded: torch.Tensor, c1: Optional[torch.Tensor],
+                           c2: torch.Tensor, *, eps: float = 1e-5, norm="layernorm", act="none",
+                           out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """y = act(rs (x @ w_folded.T - mu c1) + c2) on the outputs of
+    :func:`norm_gemm_fold_weights` (c1 may be None for RMSNorm)."""
+    if not isinstance(x, torch.Tensor) or x.dim() < 1:
+        raise ValueError("x must be a tensor with at least one dimension")
+    if x.dtype not in DTYPES:
+        raise ValueError(f"x must be float16 or bfloat16, got {x.dtype}")
+    dev = x.device
+    K = x.shape[-1]
+    M = x.numel() // K if K else 0
+    if w_folded is None or w_folded.dim() != 2 or w_folded.shape[1] != K:
+        raise ValueError(f"w_folded must be [N, {K}]")
+    N = w_folded.shape[0]
+    _check(x, "x", x.dtype, dev)
+    _check(w_folded, "w_folded", x.dtype, dev)
+    _check(c1, "c1", torch.float32, dev, (N,))
+    _check(c2, "c2", torch.float32, dev, (N,))
+    lead = tuple(x.shape[:-1])
+    if out is None:
+        out = torch.empty(lead + (N,), dtype=x.dtype, device=dev)
+    _check(out, "out", x.dtype, dev, lead + (N,))
+    with torch.cuda.device(dev):
+        st = lib.fused_norm_gemm_folded(_ptr(x), _ptr(w_folded), _ptr(c1), _ptr(c2), _ptr(out),
+                                        M, N, K, float(eps), _enum(NORMS, norm, "norm"),
+                                        _enum(ACTS, act, "act"), DTYPES[x.dtype],
+                                        _stream(dev, stream))
+    if st != 0:
+        raise NormGemmError(st, "fused_norm_gemm_folded")
     return out

@@ -177,6 +177,39 @@ int fused_ffn_noalloc(const void *x, const void *gamma, const void *beta, const 
                      (size_t)NG_FFN_NOALLOC_SCRATCH_BYTES, stream);
 }
 
+int norm_gemm_fold_weights(const void *W, const void *gamma, const void *beta, const void *bias,
+                           void *W_folded, float *c1, float *c2, int64_t N, int64_t K, int dtype,
+                           void *stream)
+{
+    int st = ng_validate_fold(W, gamma, beta, bias, W_folded, c1, c2, N, K, dtype);
+    if (st != NG_OK)
+        return st;
+    const bool vec = ng_vector_ok(K, W, gamma, beta, W_folded) != 0;
+    return ng::launch_fold(W, gamma, beta, bias, W_folded, c1, c2, N, K, dtype, vec,
+                           (hipStream_t)stream) == hipSuccess
+               ? NG_OK
+               : NG_ERR_HIP;
+}
+
+int fused_norm_gemm_folded(const void *x, const void *W_folded, const float *c1, const float *c2,
+                           void *y, int64_t M, int64_t N, int64_t K, float eps, int norm, int act,
+                           int dtype, void *stream)
+{
+    int st = ng_validate_folded(x, W_folded, c1, c2, y, M, N, K, eps, norm, act, dtype);
+    if (st != NG_OK)
+        return st;
+    ng::GemmArgs a = make_args(x, nullptr, nullptr, W_folded, nullptr, y, M, N, K, eps, norm,
+                               act, dtype);
+    a.c1 = norm == NG_NORM_LAYERNORM ? c1 : nullptr;
+    a.c2 = c2;
+    // the tiled kernel with 32-bit tile offsets, for any M
+    if (ng_route_gemm(NG_DECODE_MAX_M + 1, N, K, a.vec ? 1 : 0, ng::cu_count()) !=
+        NG_ROUTE_PREFILL_LDS)
+        return NG_ERR_UNSUPPORTED;
+    return ng::launch_prefill_lds_folded(a, (hipStream_t)stream) == hipSuccess ? NG_OK
+                                                                               : NG_ERR_HIP;
+}
+
 size_t fused_gated_ffn_workspace_size(int64_t M, int64_t F, int dtype)
 {
     return ng_gated_ffn_workspace_size(M, F, dtype);

@@ -16,6 +16,8 @@ struct GemmArgs {
     float eps;
     int norm, act, dtype;
     bool vec;  // K % 8 == 0 and x, W, gamma, beta 16-byte aligned
+    // inference-mode folding: W holds W' = W * gamma; c1 = W' 1, c2 = W beta + bias
+    const float *c1 = nullptr, *c2 = nullptr;
 };
 
 hipError_t launch_prefill(const GemmArgs &a, hipStream_t s);      // any alignment
@@ -26,6 +28,12 @@ hipError_t launch_decode_wide(const GemmArgs &a, hipStream_t s); // route NG_ROU
 // gated tiled kernel: a.W = [W_gate; W_up] is [2 a.N, a.K], a.bias [2 a.N]
 // (only when ng_gated_tiled_fits)
 hipError_t launch_prefill_lds_gated(const GemmArgs &a, hipStream_t s);
+// folded weights (a.W = W', a.c1, a.c2; route NG_ROUTE_PREFILL_LDS for any M)
+hipError_t launch_prefill_lds_folded(const GemmArgs &a, hipStream_t s);
+// W' = W * gamma, c1 = W' 1, c2 = W beta + bias (one workgroup per row of W)
+hipError_t launch_fold(const void *W, const void *gamma, const void *beta, const void *bias,
+                       void *Wf, float *c1, float *c2, int64_t N, int64_t K, int dtype, bool vec,
+                       hipStream_t s);
 // split K of the plain tiled GEMM (a.vec, no normalization): fp32 partials
 // part[ksplit][M][N], then y = act(sum of the partials + bias)
 int prefill_tiles(int64_t M, int64_t N);

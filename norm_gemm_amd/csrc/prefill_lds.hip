@@ -175,7 +175,13 @@ __global__ __launch_bounds__(256) void row_stats_to_y_kernel(const uint16_t *__r
 // computes tile b % T over the b / T-th of ksplit contiguous K ranges and
 // writes its fp32 partial sums to part[b / T][M][N] (bias and activation are
 // applied by the sum of the partials). norm selects LayerNorm or RMSNorm for
-// the in-kernel statistics (STATS == ST_PROLOGUE).
+// the in-kernel statistics (STATS == ST_PROLOGUE). FOLD: inference-mode
+// folding (page "LayerNorm 融合算子如何让大模型推理再快 15%？深度拆解 ATB 的实现",
+// section 6.2, tip 2): W holds W' = W * gamma, x goes to the MFMAs unnormalized
+// (direct loads, as without normalization), and the epilogue applies the row
+// statistics and the folded vectors: act(rs acc + (-mu rs) c1 + c2), which is
+// rs (x W'^T - mu c1) + c2 (c1 = W' 1, c2 = W beta + bias, both fp32; c1 is
+// not read for RMSNorm).
 //
 // Schedule ("ping-pong"). Waves w and w + 4 of a workgroup run on the same
 // SIMD (workgroups are dealt to SIMDs that way), and the two groups of four
@@ -192,15 +198,19 @@ __global__ __launch_bounds__(256) void row_stats_to_y_kernel(const uint16_t *__r
 // stage is read by the first group in phase 2 kt and by the second in phase
 // 2 kt + 1, so a stage is rewritten (direct loads of kt + 3, normalized x of
 // kt + 3) only from phase 2 kt + 2 on.
-template <int DT, int STATS, int GB, bool KT, bool GT, bool SK>
+template <int DT, int STATS, int GB, bool KT, bool GT, bool SK, bool FOLD>
 __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ gamma,
     const uint16_t *__restrict__ beta, const uint16_t *__restrict__ W,
     const uint16_t *__restrict__ bias, uint16_t *__restrict__ y, int M, int N, int K,
-    float eps, int norm, int act, TileMap mp, int vec_out, float *__restrict__ part, int ksplit)
+    float eps, int norm, int act, TileMap mp, int vec_out, float *__restrict__ part, int ksplit,
+    const float *__restrict__ c1, const float *__restrict__ c2)
 {
     static_assert(!SK || (STATS == ST_NONE && !GT), "split K only for the plain GEMM");
-    constexpr bool AFFINE = STATS != ST_NONE;
+    static_assert(!FOLD || (STATS == ST_FROM_Y || STATS == ST_PROLOGUE) && !GT && !SK && GB == 0,
+                  "folding: plain GEMM on raw x with row statistics");
+    // normalization inside the K loop (not with folding: x stays raw)
+    constexpr bool AFFINE = STATS != ST_NONE && !FOLD;
     // Prescaled fp16 RMSNorm (no beta): the A operand is x * 2^e * gamma,
     // rounded once to fp16, with 2^e the power of two at or below the row's
     // rs = 1/sqrt(mean(x^2) + eps) (e clamped to the fp16 normal exponents
@@ -336,10 +346,14 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
     // prescale: 2^e of this lane's x rows (packed fp16) and rs 2^-e of the
     // output rows of its accumulators (rows wm * 64 + 32 i + lrow)
     half2_t ps2[A_DMA];
-    float osc[FM];
+    // epilogue factors of the output rows of this lane's accumulators (rows
+    // wm * 64 + 32 i + lrow): v = osc acc + onm c1 + (c2 or bias)
+    float osc[FM], onm[FM];
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i) {
         osc[i] = 1.0f;
+        onm[i] = 0.0f;
+    }
     auto pow2_below = [](float rs) {
         // 2^e <= rs, e = floor(log2 rs) clamped to -14..15 (rs > 0, finite)
         int e = (int)((__builtin_bit_cast(uint32_t, rs) >> 23) & 0xffu) - 127;
@@ -355,13 +369,18 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
             rrs[i] = __builtin_bit_cast(float, pk.x);
             rnmr[i] = __builtin_bit_cast(float, pk.y);
         }
-        if constexpr (PS) {
+        if constexpr (PS || FOLD) {
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
                 const int m = min(m0 + wm * WM + i * 32 + lrow, M - 1);
-                const float rs = __builtin_bit_cast(
-                    float, *reinterpret_cast<const uint32_t *>(y + (int64_t)m * N + n0));
-                osc[i] = rs / pow2_below(rs);
+                const uint2 pk = *reinterpret_cast<const uint2 *>(y + (int64_t)m * N + n0);
+                const float rs = __builtin_bit_cast(float, pk.x);
+                if constexpr (PS) {
+                    osc[i] = rs / pow2_below(rs);
+                } else {
+                    osc[i] = rs;
+                    onm[i] = __builtin_bit_cast(float, pk.y);
+                }
             }
         }
         // complete them before the direct loads start: the compiler does not
@@ -423,6 +442,13 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
             const int row = i * A_IST + wave * 8 + (lane >> 3);
             rrs[i] = s_rs[row];
             rnmr[i] = s_nmr[row];
+        }
+        if constexpr (FOLD) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                osc[i] = s_rs[wm * WM + i * 32 + lrow];
+                onm[i] = s_nmr[wm * WM + i * 32 + lrow];
+            }
         }
         __syncthreads();
     }
@@ -829,11 +855,17 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int nl = wn * WN + j * 32 + q * 8 + lk * 4;
-                float bv[4];
+                float bv[4], cv[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int n = n0 + nl + r;
-                    bv[r] = (bias && n < N) ? bits_to_f<DT>(bias[n]) : 0.0f;
+                    if constexpr (FOLD) {
+                        bv[r] = n < N ? c2[n] : 0.0f;
+                        cv[r] = (c1 && n < N) ? c1[n] : 0.0f;
+                    } else {
+                        bv[r] = (bias && n < N) ? bits_to_f<DT>(bias[n]) : 0.0f;
+                        cv[r] = 0.0f;
+                    }
                 }
 #pragma unroll
                 for (int i = 0; i < FM; ++i) {
@@ -841,7 +873,8 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
                     float v[4];
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        v[r] = apply_act(fmaf(acc[j][i][q * 4 + r], osc[i], bv[r]), act);
+                        v[r] = apply_act(
+                            fmaf(acc[j][i][q * 4 + r], osc[i], fmaf(onm[i], cv[r], bv[r])), act);
                     const int chunk = (nl >> 3) ^ (ml & 31);
                     uint32_t *dst = reinterpret_cast<uint32_t *>(&stg[ml * 32 + chunk]) + (lk * 2);
                     dst[0] = pack2<DT>(v[0], v[1]);
@@ -872,7 +905,7 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
     }
 }
 
-template <int DT, int STATS, int GB, bool KT, bool GT, bool SK = false>
+template <int DT, int STATS, int GB, bool KT, bool GT, bool SK = false, bool FOLD = false>
 hipError_t launch_k(const GemmArgs &a, hipStream_t s, float *part = nullptr, int ksplit = 1)
 {
     const int cus = cu_count();
@@ -891,11 +924,12 @@ hipError_t launch_k(const GemmArgs &a, hipStream_t s, float *part = nullptr, int
         if (e != hipSuccess)
             return e;
     }
-    hipLaunchKernelGGL((prefill_lds_kernel<DT, STATS, GB, KT, GT, SK>), dim3(mp.T * ksplit),
+    hipLaunchKernelGGL((prefill_lds_kernel<DT, STATS, GB, KT, GT, SK, FOLD>), dim3(mp.T * ksplit),
                        dim3(THREADS), 0, s,
                        (const uint16_t *)a.x, (const uint16_t *)a.gamma, (const uint16_t *)a.beta,
                        (const uint16_t *)a.W, (const uint16_t *)a.bias, (uint16_t *)a.y, (int)a.M,
-                       (int)a.N, (int)a.K, a.eps, a.norm, a.act, mp, vec_out, part, ksplit);
+                       (int)a.N, (int)a.K, a.eps, a.norm, a.act, mp, vec_out, part, ksplit, a.c1,
+                       a.c2);
     return hipGetLastError();
 }
 
@@ -971,6 +1005,25 @@ hipError_t launch_prefill_lds_splitk(const GemmArgs &a, float *part, int ksplit,
                   : launch_k<DT_F16, ST_NONE, 0, false, false, true>(a, s, part, ksplit);
     return kt ? launch_k<DT_BF16, ST_NONE, 0, true, false, true>(a, s, part, ksplit)
               : launch_k<DT_BF16, ST_NONE, 0, false, false, true>(a, s, part, ksplit);
+}
+
+hipError_t launch_prefill_lds_folded(const GemmArgs &a, hipStream_t s)
+{
+    // a.W = W', a.c1 / a.c2 the folded vectors; statistics from the pass
+    // through y when y can hold them, else in the kernel
+    if (ng_route_gemm(NG_DECODE_MAX_M + 1, a.N, a.K, a.vec ? 1 : 0, cu_count()) !=
+            NG_ROUTE_PREFILL_LDS ||
+        a.norm == NORM_NONE || !a.c2 || (a.norm == NORM_LAYERNORM && !a.c1))
+        return hipErrorInvalidValue;
+    const bool y_scratch = a.N % 8 == 0 && ((uintptr_t)a.y & 15u) == 0;
+    const bool kt = a.K % BK != 0;
+#define NG_FOLD_K(DT, ST) \
+    (kt ? launch_k<DT, ST, 0, true, false, false, true>(a, s) \
+        : launch_k<DT, ST, 0, false, false, false, true>(a, s))
+    if (a.dtype == DT_F16)
+        return y_scratch ? NG_FOLD_K(DT_F16, ST_FROM_Y) : NG_FOLD_K(DT_F16, ST_PROLOGUE);
+    return y_scratch ? NG_FOLD_K(DT_BF16, ST_FROM_Y) : NG_FOLD_K(DT_BF16, ST_PROLOGUE);
+#undef NG_FOLD_K
 }
 
 hipError_t launch_prefill_lds_gated(const GemmArgs &a, hipStream_t s)

@@ -175,3 +175,67 @@ int ng_vector_ok(int64_t K, const void *a, const void *b, const void *c, const v
             return 0;
     return 1;
 }
+
+static int align4(const void *p)
+{
+    return ((uintptr_t)p & 3u) == 0;
+}
+
+static range_t rng_bytes(const void *p, int64_t bytes)
+{
+    range_t r;
+    r.lo = (uintptr_t)p;
+    r.hi = p ? r.lo + (uintptr_t)bytes : r.lo;
+    return r;
+}
+
+int ng_validate_fold(const void *W, const void *gamma, const void *beta, const void *bias,
+                     const void *Wf, const void *c1, const void *c2, int64_t N, int64_t K,
+                     int dtype)
+{
+    if (!W || !Wf || !c1 || !c2)
+        return NG_ERR_NULL;
+    if (dtype != NG_DTYPE_F16 && dtype != NG_DTYPE_BF16)
+        return NG_ERR_ENUM;
+    if (!dim_ok(N) || !dim_ok(K) || !mul_ok(N, K))
+        return NG_ERR_SHAPE;
+    if (!align2(W) || !align2(gamma) || !align2(beta) || !align2(bias) || !align2(Wf) ||
+        !align4(c1) || !align4(c2))
+        return NG_ERR_ALIGN;
+    /* outputs: W', c1, c2; none may overlap an input or another output */
+    range_t in[4] = {rng(W, N * K), rng(gamma, K), rng(beta, K), rng(bias, N)};
+    range_t out[3] = {rng(Wf, N * K), rng_bytes(c1, N * 4), rng_bytes(c2, N * 4)};
+    for (int o = 0; o < 3; ++o) {
+        for (int i = 0; i < 4; ++i)
+            if (overlap(out[o], in[i]))
+                return NG_ERR_ALIAS;
+        for (int p = o + 1; p < 3; ++p)
+            if (overlap(out[o], out[p]))
+                return NG_ERR_ALIAS;
+    }
+    return NG_OK;
+}
+
+int ng_validate_folded(const void *x, const void *Wf, const void *c1, const void *c2,
+                       const void *y, int64_t M, int64_t N, int64_t K, float eps, int norm,
+                       int act, int dtype)
+{
+    if (!x || !Wf || !c2 || !y || (norm == NG_NORM_LAYERNORM && !c1))
+        return NG_ERR_NULL;
+    /* folding is a normalization strategy: LayerNorm or RMSNorm only */
+    if (!enums_ok(norm, act, dtype) || norm == NG_NORM_NONE)
+        return NG_ERR_ENUM;
+    if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K) || !mul_ok(M, K) || !mul_ok(N, K) ||
+        !mul_ok(M, N))
+        return NG_ERR_SHAPE;
+    if (!eps_ok(eps, norm))
+        return NG_ERR_EPS;
+    if (!align2(x) || !align2(Wf) || !align2(y) || !align4(c1) || !align4(c2))
+        return NG_ERR_ALIGN;
+    range_t ry = rng(y, M * N);
+    if (overlap(ry, rng(x, M * K)) || overlap(ry, rng(Wf, N * K)) ||
+        overlap(ry, rng_bytes(norm == NG_NORM_LAYERNORM ? c1 : 0, N * 4)) ||
+        overlap(ry, rng_bytes(c2, N * 4)))
+        return NG_ERR_ALIAS;
+    return NG_OK;
+}

@@ -27,6 +27,18 @@ int ng_validate_gated_ffn(const void *x, const void *gamma, const void *beta, co
                           int64_t M, int64_t K, int64_t F, int64_t N, float eps, int norm,
                           int act, int dtype, const void *workspace, size_t workspace_bytes);
 
+/* Inference-mode folding: W, W' (Wf) [N,K] of dtype, gamma/beta [K], bias [N]
+ * (each optional), c1/c2 [N] fp32; outputs may overlap nothing. */
+int ng_validate_fold(const void *W, const void *gamma, const void *beta, const void *bias,
+                     const void *Wf, const void *c1, const void *c2, int64_t N, int64_t K,
+                     int dtype);
+
+/* The GEMM on folded weights: norm is LayerNorm or RMSNorm (c1 required for
+ * LayerNorm, ignored for RMSNorm), c2 required. */
+int ng_validate_folded(const void *x, const void *Wf, const void *c1, const void *c2,
+                       const void *y, int64_t M, int64_t N, int64_t K, float eps, int norm,
+                       int act, int dtype);
+
 /* 1 when every given pointer is 16-byte aligned and K % 8 == 0. */
 int ng_vector_ok(int64_t K, const void *a, const void *b, const void *c, const void *d);
 

@@ -49,7 +49,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert ng.norm_gemm_abi_version() == 4
+    assert ng.norm_gemm_abi_version() == 5
     for s in (OK, NULL, SHAPE, ENUM, EPS, ALIAS, WORKSPACE, UNSUP, ALIGN, HIP, SCRATCH):
         assert ng.norm_gemm_status_string(s)
     assert ng.norm_gemm_status_string(12345) == "unknown status"
@@ -176,3 +176,45 @@ def test_noalloc_scratch_size_matches_the_header():
     text = open(HEADER, encoding="utf-8").read()
     assert "#define NG_FFN_NOALLOC_SCRATCH_BYTES (64u << 20)" in text
     assert ng.NOALLOC_SCRATCH_BYTES == 64 << 20
+
+
+def fold(w=W, g=G, b=B, bias=BI, wf=0x90000000, c1=0xA0000000, c2=0xB0000000, N=8, K=16,
+         dtype=0):
+    return ng.lib.norm_gemm_fold_weights(w, g, b, bias, wf, c1, c2, N, K, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(w=None), NULL), (dict(wf=None), NULL), (dict(c1=None), NULL), (dict(c2=None), NULL),
+    (dict(dtype=3), ENUM), (dict(N=0), SHAPE), (dict(K=2 ** 31), SHAPE),
+    (dict(wf=0x90000001), ALIGN), (dict(c1=0xA0000002), ALIGN), (dict(g=G + 1), ALIGN),
+    (dict(wf=W + 2), ALIAS), (dict(c1=G), ALIAS), (dict(c2=0xA0000000 + 16), ALIAS),
+    (dict(c2=0x90000000 + 8 * 16 * 2 - 4), ALIAS),
+])
+@no_gpu_only
+def test_fold_weights_validation_errors(kw, status):
+    assert fold(**kw) == status
+
+
+def folded(x=X, wf=W, c1=0xA0000000, c2=0xB0000000, y=Y, M=4, N=8, K=16, eps=1e-5, norm=1,
+           act=0, dtype=0):
+    return ng.lib.fused_norm_gemm_folded(x, wf, c1, c2, y, M, N, K, eps, norm, act, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), NULL), (dict(c2=None), NULL), (dict(c1=None, norm=1), NULL),
+    (dict(norm=0), ENUM), (dict(norm=3), ENUM), (dict(act=7), ENUM), (dict(M=0), SHAPE),
+    (dict(eps=-1.0), EPS), (dict(y=Y + 1), ALIGN), (dict(c2=0xB0000001), ALIGN),
+    (dict(y=X), ALIAS), (dict(y=0xB0000000 - 4), ALIAS), (dict(y=W + 6), ALIAS),
+    # unaligned x or K % 8 != 0: the tiled kernel cannot serve the call
+    (dict(x=X + 2), UNSUP), (dict(K=20), UNSUP),
+])
+@no_gpu_only
+def test_fused_norm_gemm_folded_validation_errors(kw, status):
+    assert folded(**kw) == status
+
+
+@no_gpu_only
+def test_folded_rmsnorm_does_not_need_c1():
+    # RMSNorm ignores c1, so a NULL c1 is valid; K % 8 != 0 then stops the
+    # call before any launch
+    assert folded(c1=None, norm=2, K=20) == UNSUP
