@@ -82,6 +82,9 @@ def lib():
                                               ctypes.c_float, ctypes.c_int, ctypes.c_int,
                                               ctypes.c_int, pi64, i64, pi64, i64, pf64]
         L.oracle_norm_gemm_folded.restype = ctypes.c_int
+        L.oracle_gemm_norm.argtypes = [p16, p16, p16, p16, p16, i64, i64, i64, ctypes.c_float,
+                                       ctypes.c_int, ctypes.c_int, pi64, i64, pi64, i64, pf64]
+        L.oracle_gemm_norm.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -238,4 +241,26 @@ def norm_gemm_folded(x, Wf, c1, c2, eps: float, norm: int, act: int, dtype: int,
                                        out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
     if rc != 0:
         raise ValueError(f"oracle_norm_gemm_folded failed ({rc})")
+    return out
+
+
+def gemm_norm(x, W, bias, gamma, beta, eps: float, norm: int, dtype: int,
+              rows: Optional[Sequence[int]] = None,
+              cols: Optional[Sequence[int]] = None) -> np.ndarray:
+    """y = norm_affine(x W^T + bias) over each output row (gamma, beta [N])."""
+    M, K = x.shape
+    N = W.shape[0]
+    assert W.shape[1] == K
+    x, px = _u16(x)
+    w, pw = _u16(W)
+    bi, pbi = _u16(bias)
+    g, pg = _u16(gamma)
+    b, pb = _u16(beta)
+    r, pr = _idx(rows, M)
+    c, pc = _idx(cols, N)
+    out = np.empty((len(r), len(c)), dtype=np.float64)
+    rc = lib().oracle_gemm_norm(px, pw, pbi, pg, pb, M, N, K, eps, norm, dtype, pr, len(r),
+                                pc, len(c), out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
+    if rc != 0:
+        raise ValueError(f"oracle_gemm_norm failed ({rc})")
     return out

@@ -407,3 +407,68 @@ int oracle_norm_gemm_folded(const uint16_t *x, const double *Wf, const double *c
     }
     return OR_OK;
 }
+
+/* Post-GEMM normalization (page "昇腾CANN的MatMul融合玩法，让大模型推理快3倍",
+ * section 五, optimization 3: the fused "MatMul(Output)_RMSNorm" of the LLaMA
+ * layer, the attention output projection followed by the RMSNorm). The pages
+ * give no formula; read as the normalization of each output row of the GEMM:
+ *   z[m,n] = sum_k x[m,k] W[n,k] + bias[n]
+ *   RMSNorm:   y[m,n] = z[m,n] / sqrt(mean_n z[m,n]^2 + eps) * gamma[n] + beta[n]
+ *   LayerNorm: y[m,n] = (z[m,n] - mu_m) / sqrt(var_m + eps) * gamma[n] + beta[n]
+ *              (mean and biased variance over the N outputs of the row)
+ * gamma/beta/bias are [N]; NULL means 1 / 0 / 0. The statistics need every
+ * output of a row, so each requested row is computed in full (fp64). */
+int oracle_gemm_norm(const uint16_t *x, const uint16_t *W, const uint16_t *bias,
+                     const uint16_t *gamma, const uint16_t *beta, int64_t M, int64_t N,
+                     int64_t K, float eps, int norm, int dtype, const int64_t *rows,
+                     int64_t n_rows, const int64_t *cols, int64_t n_cols, double *y_out)
+{
+    if (check_common(M, K, norm, OR_ACT_NONE, dtype) || N < 1 || norm == OR_NORM_NONE || !x ||
+        !W || !rows || !cols || !y_out)
+        return OR_ERR_ARG;
+    for (int64_t i = 0; i < n_rows; ++i)
+        if (rows[i] < 0 || rows[i] >= M)
+            return OR_ERR_ARG;
+    for (int64_t j = 0; j < n_cols; ++j)
+        if (cols[j] < 0 || cols[j] >= N)
+            return OR_ERR_ARG;
+    double *z = (double *)malloc(sizeof(double) * (size_t)N);
+    if (!z)
+        return OR_ERR_NOMEM;
+    const double e = (double)eps;
+    for (int64_t i = 0; i < n_rows; ++i) {
+        const uint16_t *xr = x + rows[i] * K;
+#pragma omp parallel for schedule(dynamic, 16)
+        for (int64_t n = 0; n < N; ++n) {
+            const uint16_t *wr = W + n * K;
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k)
+                acc += dec(xr[k], dtype) * dec(wr[k], dtype);
+            z[n] = acc + (bias ? dec(bias[n], dtype) : 0.0);
+        }
+        double mu = 0.0, r;
+        if (norm == OR_NORM_LAYERNORM) {
+            double sz = 0.0, q = 0.0;
+            for (int64_t n = 0; n < N; ++n)
+                sz += z[n];
+            mu = sz / (double)N;
+            for (int64_t n = 0; n < N; ++n)
+                q += (z[n] - mu) * (z[n] - mu);
+            r = 1.0 / sqrt(q / (double)N + e);
+        } else {
+            double q = 0.0;
+            for (int64_t n = 0; n < N; ++n)
+                q += z[n] * z[n];
+            r = 1.0 / sqrt(q / (double)N + e);
+        }
+        for (int64_t j = 0; j < n_cols; ++j) {
+            const int64_t n = cols[j];
+            double g = gamma ? dec(gamma[n], dtype) : 1.0;
+            double b = beta ? dec(beta[n], dtype) : 0.0;
+            y_out[i * n_cols + j] = (z[n] - mu) * r * g + b;
+        }
+    }
+    free(z);
+    return OR_OK;
+}
+

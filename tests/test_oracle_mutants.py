@@ -47,9 +47,19 @@ FOLD_MUTATIONS = {
     "fold_gamma_dropped": ("double wf = w * g;", "double wf = w;"),
     "fold_c1_of_unfolded_w": ("s1 += wf;", "s1 += w;"),
 }
+# Mistakes in the post-GEMM normalization, caught by its own pins.
+POSTNORM_MUTATIONS = {
+    "postnorm_uncentred_variance": ("q += (z[n] - mu) * (z[n] - mu);", "q += z[n] * z[n];"),
+    "postnorm_rms_of_abs": ("q += z[n] * z[n];", "q += fabs(z[n]);"),
+    "postnorm_no_bias": ("z[n] = acc + (bias ? dec(bias[n], dtype) : 0.0);", "z[n] = acc;"),
+    "postnorm_gamma_ignored": ("y_out[i * n_cols + j] = (z[n] - mu) * r * g + b;",
+                               "y_out[i * n_cols + j] = (z[n] - mu) * r + b;"),
+}
 PIN_FILE = {name: "test_oracle_pins.py" for name in MUTATIONS}
 PIN_FILE.update({name: "test_oracle_fold.py" for name in FOLD_MUTATIONS})
+PIN_FILE.update({name: "test_oracle_postnorm.py" for name in POSTNORM_MUTATIONS})
 MUTATIONS.update(FOLD_MUTATIONS)
+MUTATIONS.update(POSTNORM_MUTATIONS)
 
 
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
