@@ -341,13 +341,13 @@ int oracle_fold_weights(const uint16_t *W, const uint16_t *gamma, const uint16_t
         double s1 = 0.0, s2 = 0.0;
         for (int64_t k = 0; k < K; ++k) {
             double w = dec(W[n * K + k], dtype);
-            double g = gamma ? dec(gamma[k], dtype) : 1.0;
-            double b = beta ? dec(beta[k], dtype) : 0.0;
-            double wf = w * g;
+            double gk = gamma ? dec(gamma[k], dtype) : 1.0;
+            double bk = beta ? dec(beta[k], dtype) : 0.0;
+            double wf = w * gk;
             if (Wf)
                 Wf[n * K + k] = wf;
             s1 += wf;
-            s2 += w * b;
+            s2 += w * bk;
         }
         c1[n] = s1;
         c2[n] = s2 + (bias ? dec(bias[n], dtype) : 0.0);

@@ -44,7 +44,7 @@ FOLD_MUTATIONS = {
     "fold_c1_sign": ("y_out[t] = apply_act(r * (acc - mu * c1[cols[j]]) + c2[cols[j]], act);",
                      "y_out[t] = apply_act(r * (acc + mu * c1[cols[j]]) + c2[cols[j]], act);"),
     "fold_c2_without_bias": ("c2[n] = s2 + (bias ? dec(bias[n], dtype) : 0.0);", "c2[n] = s2;"),
-    "fold_gamma_dropped": ("double wf = w * g;", "double wf = w;"),
+    "fold_gamma_dropped": ("double wf = w * gk;", "double wf = w;"),
     "fold_c1_of_unfolded_w": ("s1 += wf;", "s1 += w;"),
 }
 # Mistakes in the post-GEMM normalization, caught by its own pins.
