@@ -50,7 +50,8 @@ HEADLINE = "rms_matmul_silu_512x14336"
 # (inference mode), the folding itself done once before the timed region
 EXTRAS = ("ffn_silu_512x14336x49152", "ln_linear_bias_1024x8192", "decode_rms_gemm_m1",
           "decode_rms_gemm_m8", "decode_rms_gemm_m32", "ln_linear_bias_64x256",
-          "rms_matmul_silu_512x14336:folded", "ln_linear_bias_1024x8192:folded")
+          "rms_matmul_silu_512x14336:folded", "ln_linear_bias_1024x8192:folded",
+          "attn_out_rmsnorm_512x8192")
 
 
 def workload(name: str):
@@ -110,6 +111,8 @@ def algorithmic(case):
 
 
 def launches_per_step(case) -> int:
+    if case.kind == "gemm_norm":
+        return 2
     is_ffn = case.kind in ("ffn", "gated_ffn")
     return (2 if is_ffn else 1) + (1 if case.norm and case.M > 32 else 0)
 
@@ -146,6 +149,9 @@ def measure(name: str, steps: int, warmup: int):
     ws = None
     if is_ffn:
         ws = torch.empty(ws_size(case.M, case.F, up["x"].dtype), dtype=torch.uint8, device=dev)
+    elif case.kind == "gemm_norm":
+        ws = torch.empty(2 * ng.fused_gemm_norm_workspace_size(case.M, case.N),
+                         dtype=torch.uint8, device=dev)
 
     def step(i):
         w = wsets[i % copies]
@@ -153,6 +159,9 @@ def measure(name: str, steps: int, warmup: int):
             ffn_call(get("x"), w["W1"], w["W2"], get("gamma"), get("beta"), get("b1"),
                      get("b2"), eps=case.eps, norm=case.norm, act=case.act,
                      workspace=ws, out=out)
+        elif case.kind == "gemm_norm":
+            ng.fused_gemm_norm(get("x"), w["W"], get("bias"), get("gamma"), get("beta"),
+                               eps=case.eps, norm=case.norm, workspace=ws, out=out)
         elif folded:
             ng.fused_norm_gemm_folded(get("x"), w["W"], w["c1"], w["c2"], eps=case.eps,
                                       norm=case.norm, act=case.act, out=out)

@@ -62,7 +62,8 @@ extern "C" {
 
 #define NORM_GEMM_ABI_VERSION 5   /* 2: NG_ACT_RELU, NG_ACT_GELU; 3: fused_gated_ffn;
                                      4: fused_ffn_noalloc, NG_ERR_SCRATCH;
-                                     5: norm_gemm_fold_weights, fused_norm_gemm_folded */
+                                     5: norm_gemm_fold_weights, fused_norm_gemm_folded,
+                                        fused_gemm_norm */
 
 typedef enum { NG_NORM_NONE = 0, NG_NORM_LAYERNORM = 1, NG_NORM_RMSNORM = 2 } ng_norm_t;
 typedef enum { NG_ACT_NONE = 0, NG_ACT_SILU = 1, NG_ACT_RELU = 2, NG_ACT_GELU = 3 } ng_act_t;
@@ -191,6 +192,33 @@ int norm_gemm_fold_weights(const void *W, const void *gamma, const void *beta,
 int fused_norm_gemm_folded(const void *x, const void *W_folded, const float *c1,
                            const float *c2, void *y, int64_t M, int64_t N, int64_t K,
                            float eps, int norm, int act, int dtype, void *stream);
+
+/*
+ * Post-GEMM normalization (page "昇腾CANN的MatMul融合玩法，让大模型推理快3倍",
+ * section 五, optimization 3: the fused "MatMul(Output)_RMSNorm" of the LLaMA
+ * layer, the attention output projection followed by its RMSNorm):
+ *
+ *     z[m,n] = sum_k x[m,k] W[n,k] + bias[n]
+ *     y[m,n] = (z[m,n] - mu_m) / sqrt(var_m + eps) * gamma[n] + beta[n]
+ *
+ * with the statistics over the N outputs of row m: RMSNorm mu = 0 and var =
+ * mean of z^2; LayerNorm the mean and the biased variance (norm = NONE is
+ * NG_ERR_ENUM). bias, gamma, beta are [N]; NULL means 0 / 1 / 0. The sums z
+ * are kept in fp32 in the workspace (a 16-byte aligned device buffer of at
+ * least fused_gemm_norm_workspace_size(M, N) = 4 M N bytes rounded up to 256;
+ * twice that lets the GEMM split K over two workgroups per tile when its
+ * tiles fill at most half of the CUs); a second kernel adds the bias, takes
+ * the row statistics in two passes and writes y rounded once. Two kernels
+ * on `stream`, no synchronization. x and W must be 16-byte aligned with K % 8
+ * == 0 and K <= 8,388,600 (the tiled kernel, any M), else NG_ERR_UNSUPPORTED.
+ * Other conventions as fused_ffn (workspace checked for size and overlaps).
+ */
+size_t fused_gemm_norm_workspace_size(int64_t M, int64_t N);
+
+int fused_gemm_norm(const void *x, const void *W, const void *bias, const void *gamma,
+                    const void *beta, void *y, int64_t M, int64_t N, int64_t K,
+                    float eps, int norm, int dtype, void *workspace,
+                    size_t workspace_bytes, void *stream);
 
 /*
  * fused_ffn_noalloc: fused_ffn for callers that cannot allocate device memory

@@ -9,6 +9,7 @@ supplies device memory and the stream. The functions mirror the C ABI in
 * :func:`fused_ffn_noalloc` -- the FFN with the library's static workspace
 * :func:`norm_gemm_fold_weights`, :func:`fused_norm_gemm_folded` --
   inference-mode folding of gamma / beta into the weights
+* :func:`fused_gemm_norm` -- y = norm_affine(x @ W.T + bias) over output rows
 * :func:`fused_ffn_workspace_size`, :func:`norm_gemm_status_string`,
   :func:`norm_gemm_abi_version`
 
@@ -35,7 +36,8 @@ DTYPES = {torch.float16: 0, torch.bfloat16: 1}
 # Symbols declared in include/norm_gemm.h.
 EXPORTED = ("fused_norm_gemm", "fused_ffn", "fused_ffn_workspace_size", "fused_gated_ffn",
             "fused_gated_ffn_workspace_size", "fused_ffn_noalloc", "norm_gemm_fold_weights",
-            "fused_norm_gemm_folded", "norm_gemm_status_string", "norm_gemm_abi_version")
+            "fused_norm_gemm_folded", "fused_gemm_norm", "fused_gemm_norm_workspace_size",
+            "norm_gemm_status_string", "norm_gemm_abi_version")
 
 # Size of the static device array behind fused_ffn_noalloc
 # (NG_FFN_NOALLOC_SCRATCH_BYTES in include/norm_gemm.h).
@@ -71,6 +73,10 @@ def _load() -> ctypes.CDLL:
     L.norm_gemm_fold_weights.restype = ci
     L.fused_norm_gemm_folded.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, f32, ci, ci, ci, vp]
     L.fused_norm_gemm_folded.restype = ci
+    L.fused_gemm_norm_workspace_size.argtypes = [i64, i64]
+    L.fused_gemm_norm_workspace_size.restype = sz
+    L.fused_gemm_norm.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, f32, ci, ci, vp, sz, vp]
+    L.fused_gemm_norm.restype = ci
     L.norm_gemm_status_string.argtypes = [ci]
     L.norm_gemm_status_string.restype = ctypes.c_char_p
     L.norm_gemm_abi_version.argtypes = []
@@ -313,4 +319,50 @@ def fused_norm_gemm_folded(x: torch.Tensor, w_folded: torch.Tensor, c1: Optional
                                         _stream(dev, stream))
     if st != 0:
         raise NormGemmError(st, "fused_norm_gemm_folded")
+    return out
+
+
+def fused_gemm_norm_workspace_size(M: int, N: int) -> int:
+    return int(lib.fused_gemm_norm_workspace_size(int(M), int(N)))
+
+
+def fused_gemm_norm(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                    gamma: Optional[torch.Tensor] = None, beta: Optional[torch.Tensor] = None, *,
+                    eps: float = 1e-5, norm="rmsnorm", workspace: Optional[torch.Tensor] = None,
+                    out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """y = norm_affine(x @ weight.T + bias) over each output row (gamma, beta,
+    bias of length N). The fp32 sums live in ``workspace`` (uint8, at least
+    :func:`fused_gemm_norm_workspace_size` bytes; twice that lets K split;
+    allocated at twice that size when not given)."""
+    if not isinstance(x, torch.Tensor) or x.dim() < 1:
+        raise ValueError("x must be a tensor with at least one dimension")
+    if x.dtype not in DTYPES:
+        raise ValueError(f"x must be float16 or bfloat16, got {x.dtype}")
+    dev = x.device
+    K = x.shape[-1]
+    M = x.numel() // K if K else 0
+    if weight is None or weight.dim() != 2 or weight.shape[1] != K:
+        raise ValueError(f"weight must be [N, {K}]")
+    N = weight.shape[0]
+    _check(x, "x", x.dtype, dev)
+    _check(weight, "weight", x.dtype, dev)
+    for t, name in ((bias, "bias"), (gamma, "gamma"), (beta, "beta")):
+        _check(t, name, x.dtype, dev, (N,))
+    if workspace is None:
+        workspace = torch.empty(2 * fused_gemm_norm_workspace_size(M, N), dtype=torch.uint8,
+                                device=dev)
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on x's device")
+    lead = tuple(x.shape[:-1])
+    if out is None:
+        out = torch.empty(lead + (N,), dtype=x.dtype, device=dev)
+    _check(out, "out", x.dtype, dev, lead + (N,))
+    with torch.cuda.device(dev):
+        st = lib.fused_gemm_norm(_ptr(x), _ptr(weight), _ptr(bias), _ptr(gamma), _ptr(beta),
+                                 _ptr(out), M, N, K, float(eps), _enum(NORMS, norm, "norm"),
+                                 DTYPES[x.dtype], _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(),
+                                 _stream(dev, stream))
+    if st != 0:
+        raise NormGemmError(st, "fused_gemm_norm")
     return out

@@ -210,6 +210,42 @@ int fused_norm_gemm_folded(const void *x, const void *W_folded, const float *c1,
                                                                                : NG_ERR_HIP;
 }
 
+size_t fused_gemm_norm_workspace_size(int64_t M, int64_t N)
+{
+    return ng_gemm_norm_workspace_size(M, N);
+}
+
+int fused_gemm_norm(const void *x, const void *W, const void *bias, const void *gamma,
+                    const void *beta, void *y, int64_t M, int64_t N, int64_t K, float eps,
+                    int norm, int dtype, void *workspace, size_t workspace_bytes, void *stream)
+{
+    int st = ng_validate_gemm_norm(x, W, bias, gamma, beta, y, M, N, K, eps, norm, dtype,
+                                   workspace, workspace_bytes);
+    if (st != NG_OK)
+        return st;
+    const ng::GemmArgs a = make_args(x, nullptr, nullptr, W, nullptr, y, M, N, K, 0.0f,
+                                     NG_NORM_NONE, NG_ACT_NONE, dtype);
+    // the tiled kernel writes the fp32 sums, for any M
+    if (ng_route_gemm(NG_DECODE_MAX_M + 1, N, K, a.vec ? 1 : 0, ng::cu_count()) !=
+        NG_ROUTE_PREFILL_LDS)
+        return NG_ERR_UNSUPPORTED;
+    hipStream_t s = (hipStream_t)stream;
+    // K split over two workgroups per tile when the tiles fill at most half of
+    // the CUs and the workspace holds two planes
+    const size_t plane = ng_gemm_norm_workspace_size(M, N);
+    const int ksplit = (2 * ng::prefill_tiles(M, N) <= ng::cu_count() &&
+                        ng::prefill_k_steps(K) >= 4 && workspace_bytes >= 2 * plane)
+                           ? 2
+                           : 1;
+    // the planes are M N floats apart: with ksplit 2 the partial of range s
+    // starts at s M N (the sum kernel's layout), inside the two planes
+    if (ng::launch_prefill_lds_splitk(a, (float *)workspace, ksplit, s) != hipSuccess ||
+        ng::launch_postnorm((const float *)workspace, bias, gamma, beta, y, M, N, ksplit, eps,
+                            norm, dtype, s) != hipSuccess)
+        return NG_ERR_HIP;
+    return NG_OK;
+}
+
 size_t fused_gated_ffn_workspace_size(int64_t M, int64_t F, int dtype)
 {
     return ng_gated_ffn_workspace_size(M, F, dtype);

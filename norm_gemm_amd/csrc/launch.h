@@ -35,12 +35,16 @@ hipError_t launch_fold(const void *W, const void *gamma, const void *beta, const
                        void *Wf, float *c1, float *c2, int64_t N, int64_t K, int dtype, bool vec,
                        hipStream_t s);
 // split K of the plain tiled GEMM (a.vec, no normalization): fp32 partials
-// part[ksplit][M][N], then y = act(sum of the partials + bias)
+// part[ksplit][M][N] (ksplit >= 1), then y = act(sum of the partials + bias)
 int prefill_tiles(int64_t M, int64_t N);
 int prefill_k_steps(int64_t K);
 hipError_t launch_prefill_lds_splitk(const GemmArgs &a, float *part, int ksplit, hipStream_t s);
 hipError_t launch_splitk_sum(const float *part, const void *bias, void *y, int64_t M, int64_t N,
                              int ksplit, int act, int dtype, hipStream_t s);
+// y = norm_affine(sum of the partials + bias) over each output row
+hipError_t launch_postnorm(const float *part, const void *bias, const void *gamma,
+                           const void *beta, void *y, int64_t M, int64_t N, int ksplit, float eps,
+                           int norm, int dtype, hipStream_t s);
 // h[M, F] = act(gu[:, :F]) * gu[:, F:] for gu[M, 2F]
 hipError_t launch_gate(const void *gu, void *h, int64_t M, int64_t F, int act, int dtype,
                        hipStream_t s);

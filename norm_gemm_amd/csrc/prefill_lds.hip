@@ -995,9 +995,11 @@ int prefill_k_steps(int64_t K)
 hipError_t launch_prefill_lds_splitk(const GemmArgs &a, float *part, int ksplit,
                                      hipStream_t s)
 {
-    // plain GEMM only; every K range must get at least one step
-    if (ng_route_gemm(a.M, a.N, a.K, a.vec ? 1 : 0, cu_count()) != NG_ROUTE_PREFILL_LDS ||
-        a.norm != NORM_NONE || ksplit < 2 || prefill_k_steps(a.K) < 2 * ksplit)
+    // plain GEMM only, any M; every K range must get at least one step (one
+    // range writes the fp32 sums of the whole K)
+    if (ng_route_gemm(NG_DECODE_MAX_M + 1, a.N, a.K, a.vec ? 1 : 0, cu_count()) !=
+            NG_ROUTE_PREFILL_LDS ||
+        a.norm != NORM_NONE || ksplit < 1 || (ksplit > 1 && prefill_k_steps(a.K) < 2 * ksplit))
         return hipErrorInvalidValue;
     const bool kt = a.K % BK != 0;
     if (a.dtype == DT_F16)

@@ -239,3 +239,47 @@ int ng_validate_folded(const void *x, const void *Wf, const void *c1, const void
         return NG_ERR_ALIAS;
     return NG_OK;
 }
+
+size_t ng_gemm_norm_workspace_size(int64_t M, int64_t N)
+{
+    if (!dim_ok(M) || !dim_ok(N) || !mul_ok(M, N) || (size_t)M * (size_t)N > SIZE_MAX / 8u)
+        return 0;
+    return (((size_t)M * (size_t)N * 4u) + 255u) & ~(size_t)255u;
+}
+
+int ng_validate_gemm_norm(const void *x, const void *W, const void *bias, const void *gamma,
+                          const void *beta, const void *y, int64_t M, int64_t N, int64_t K,
+                          float eps, int norm, int dtype, const void *workspace,
+                          size_t workspace_bytes)
+{
+    if (!x || !W || !y)
+        return NG_ERR_NULL;
+    if (!enums_ok(norm, NG_ACT_NONE, dtype) || norm == NG_NORM_NONE)
+        return NG_ERR_ENUM;
+    if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K) || !mul_ok(M, K) || !mul_ok(N, K) ||
+        !mul_ok(M, N))
+        return NG_ERR_SHAPE;
+    if (!eps_ok(eps, norm))
+        return NG_ERR_EPS;
+    if (!align2(x) || !align2(W) || !align2(bias) || !align2(gamma) || !align2(beta) ||
+        !align2(y) || ((uintptr_t)workspace & 15u) != 0)
+        return NG_ERR_ALIGN;
+    range_t in[5] = {rng(x, M * K), rng(W, N * K), rng(bias, N), rng(gamma, N), rng(beta, N)};
+    range_t ry = rng(y, M * N);
+    for (int i = 0; i < 5; ++i)
+        if (overlap(ry, in[i]))
+            return NG_ERR_ALIAS;
+    const size_t need = ng_gemm_norm_workspace_size(M, N);
+    if (!workspace || need == 0 || workspace_bytes < need)
+        return NG_ERR_WORKSPACE;
+    /* bytes the library may touch: one fp32 plane of the sums, or two when
+     * the workspace holds them (split K) */
+    const size_t touch = workspace_bytes >= 2u * need ? 2u * need : need;
+    range_t rw = rng_bytes(workspace, (int64_t)touch);
+    if (overlap(rw, ry))
+        return NG_ERR_ALIAS;
+    for (int i = 0; i < 5; ++i)
+        if (overlap(rw, in[i]))
+            return NG_ERR_ALIAS;
+    return NG_OK;
+}

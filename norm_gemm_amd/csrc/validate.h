@@ -39,6 +39,15 @@ int ng_validate_folded(const void *x, const void *Wf, const void *c1, const void
                        const void *y, int64_t M, int64_t N, int64_t K, float eps, int norm,
                        int act, int dtype);
 
+/* Post-GEMM normalization: norm is LayerNorm or RMSNorm; bias, gamma, beta
+ * [N] optional; the workspace (16-byte aligned) holds at least one fp32 plane
+ * of the M x N sums (ng_gemm_norm_workspace_size). */
+int ng_validate_gemm_norm(const void *x, const void *W, const void *bias, const void *gamma,
+                          const void *beta, const void *y, int64_t M, int64_t N, int64_t K,
+                          float eps, int norm, int dtype, const void *workspace,
+                          size_t workspace_bytes);
+size_t ng_gemm_norm_workspace_size(int64_t M, int64_t N);
+
 /* 1 when every given pointer is 16-byte aligned and K % 8 == 0. */
 int ng_vector_ok(int64_t K, const void *a, const void *b, const void *c, const void *d);
 

@@ -189,6 +189,9 @@ def ffn(x, gamma, beta, W1, b1, W2, b2, eps: float, norm: int, act: int, dtype: 
 def run_case(case, rows=None, cols=None) -> np.ndarray:
     """Oracle output for a :class:`synth.Case` (optionally a row/col sample)."""
     A = case.arrays
+    if case.kind == "gemm_norm":
+        return gemm_norm(A["x"], A["W"], A.get("bias"), A.get("gamma"), A.get("beta"),
+                         case.eps, case.norm, case.dtype, rows, cols)
     if case.kind in ("ffn", "gated_ffn"):
         return ffn(A["x"], A.get("gamma"), A.get("beta"), A["W1"], A.get("b1"),
                    A["W2"], A.get("b2"), case.eps, case.norm, case.act, case.dtype,

@@ -13,8 +13,9 @@ Recipe (stated once here and in the design notes):
   bf16 via :func:`f32_to_bf16_bits`).
 * ``N(a, b)`` is read as mean ``a`` and *variance* ``b``: weights use the
   fan-in variance ``1/K``, so their std is ``K**-0.5``.
-* Draw order per case: x, gamma, beta, W (or W1, W2), bias (or b1, b2);
-  tensors a case does not have are not drawn.
+* Draw order per case: x, gamma, beta, W (or W1, W2), bias (or b1, b2); for
+  the post-GEMM normalization, whose gamma / beta act on the output row: x, W,
+  bias, gamma, beta. Tensors a case does not have are not drawn.
 * Large tensors are drawn in fixed-size chunks from the same stream, which
   yields the same values as one draw of the whole tensor.
 """
@@ -80,7 +81,7 @@ def normal_bits(rng: np.random.Generator, shape, mean: float, var: float,
 class Case:
     """One workload: shapes, options and the input bit patterns (uint16)."""
     name: str
-    kind: str                      # "norm_gemm" or "ffn"
+    kind: str                      # "norm_gemm", "ffn", "gated_ffn" or "gemm_norm"
     dtype: int
     M: int
     K: int
@@ -148,6 +149,21 @@ def make_gated_ffn(name: str, M: int, K: int, F: int, N: int, *, dtype: int = F1
     return Case(name, "gated_ffn", dtype, M, K, N, F, norm, act, eps, arr)
 
 
+def make_gemm_norm(name: str, M: int, K: int, N: int, *, dtype: int = F16,
+                   norm: int = NORM_RMSNORM, eps: float = 1e-5, bias: bool = False,
+                   gamma: bool = True, beta: bool = False, seed: int = 0) -> Case:
+    """Post-GEMM normalization: x[M,K] ~ N(0,1), W[N,K] ~ N(0, 1/K), then the
+    output row's bias[N] ~ N(0, 0.1), gamma[N] ~ N(1, 0.1), beta[N] ~ N(0, 0.1)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    arr: Dict[str, Optional[np.ndarray]] = {}
+    arr["x"] = normal_bits(rng, (M, K), 0.0, 1.0, dtype)
+    arr["W"] = normal_bits(rng, (N, K), 0.0, 1.0 / K, dtype)
+    arr["bias"] = normal_bits(rng, (N,), 0.0, 0.1, dtype) if bias else None
+    arr["gamma"] = normal_bits(rng, (N,), 1.0, 0.1, dtype) if gamma else None
+    arr["beta"] = normal_bits(rng, (N,), 0.0, 0.1, dtype) if beta else None
+    return Case(name, "gemm_norm", dtype, M, K, N, 0, norm, ACT_NONE, eps, arr)
+
+
 # The five workloads of the hot path, by what they are.
 def ln_linear_bias_64x256(seed: int = 0) -> Case:
     return make_norm_gemm("ln_linear_bias_x64x256_w256x256_f16", 64, 256, 256,
@@ -177,6 +193,14 @@ def gated_ffn_swiglu_512x8192x28672(seed: int = 0) -> Case:
                           seed=seed)
 
 
+def attn_out_rmsnorm_512x8192(seed: int = 0) -> Case:
+    """The attention output projection with the RMSNorm after it (LLaMA-2-70B
+    hidden size 8192, 512 tokens): x[512, 8192] . W[8192, 8192]^T, then
+    RMSNorm with gamma over the 8192 outputs, fp16."""
+    return make_gemm_norm("attn_out_rmsnorm_x512x8192_w8192x8192_f16", 512, 8192, 8192,
+                          norm=NORM_RMSNORM, eps=1e-5, gamma=True, seed=seed)
+
+
 def decode_rms_gemm_8192x28672(M: int, seed: int = 0) -> Case:
     return make_norm_gemm(f"decode_rms_gemm_m{M}_x{M}x8192_w28672x8192_bf16", M,
                           8192, 28672, dtype=BF16, norm=NORM_RMSNORM,
@@ -189,6 +213,7 @@ WORKLOADS = {
     "rms_matmul_silu_512x14336": rms_matmul_silu_512x14336,
     "ffn_silu_512x14336x49152": ffn_silu_512x14336x49152,
     "gated_ffn_swiglu_512x8192x28672": gated_ffn_swiglu_512x8192x28672,
+    "attn_out_rmsnorm_512x8192": attn_out_rmsnorm_512x8192,
     "decode_rms_gemm_m1": lambda seed=0: decode_rms_gemm_8192x28672(1, seed),
     "decode_rms_gemm_m8": lambda seed=0: decode_rms_gemm_8192x28672(8, seed),
     "decode_rms_gemm_m32": lambda seed=0: decode_rms_gemm_8192x28672(32, seed),

@@ -50,6 +50,9 @@ def run_case_gpu(case, device="cuda"):
     if case.kind == "gated_ffn":
         return ng.fused_gated_ffn(up("x"), up("W1"), up("W2"), up("gamma"), up("beta"), up("b1"),
                                   up("b2"), eps=case.eps, norm=norm, act=act)
+    if case.kind == "gemm_norm":
+        return ng.fused_gemm_norm(up("x"), up("W"), up("bias"), up("gamma"), up("beta"),
+                                  eps=case.eps, norm=norm)
     if case.kind == "ffn":
         return ng.fused_ffn(up("x"), up("W1"), up("W2"), up("gamma"), up("beta"), up("b1"),
                             up("b2"), eps=case.eps, norm=norm, act=act)

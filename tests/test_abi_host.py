@@ -218,3 +218,30 @@ def test_folded_rmsnorm_does_not_need_c1():
     # RMSNorm ignores c1, so a NULL c1 is valid; K % 8 != 0 then stops the
     # call before any launch
     assert folded(c1=None, norm=2, K=20) == UNSUP
+
+
+def gnorm(x=X, w=W, bias=BI, g=G, b=B, y=Y, M=4, N=8, K=16, eps=1e-5, norm=2, dtype=0, ws=WS,
+          wsb=256):
+    return ng.lib.fused_gemm_norm(x, w, bias, g, b, y, M, N, K, eps, norm, dtype, ws, wsb, None)
+
+
+def test_gemm_norm_workspace_size():
+    assert ng.fused_gemm_norm_workspace_size(512, 8192) == 4 * 512 * 8192
+    assert ng.fused_gemm_norm_workspace_size(3, 5) == 256
+    assert ng.fused_gemm_norm_workspace_size(0, 5) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), NULL), (dict(y=None), NULL), (dict(norm=0), ENUM), (dict(dtype=2), ENUM),
+    (dict(N=0), SHAPE), (dict(eps=float("nan")), EPS), (dict(ws=WS + 8), ALIGN),
+    (dict(g=G + 1), ALIGN), (dict(y=X + 16), ALIAS), (dict(y=G - 8), ALIAS),
+    (dict(ws=None), WORKSPACE), (dict(wsb=255), WORKSPACE), (dict(ws=Y), ALIAS),
+    (dict(ws=W + 32), ALIAS),
+    # a workspace of two planes is alias-checked over both
+    (dict(wsb=512, y=WS + 300), ALIAS),
+    # unaligned x or K % 8 != 0: the tiled kernel cannot serve the call
+    (dict(x=X + 2), UNSUP), (dict(K=12), UNSUP),
+])
+@no_gpu_only
+def test_fused_gemm_norm_validation_errors(kw, status):
+    assert gnorm(**kw) == status
