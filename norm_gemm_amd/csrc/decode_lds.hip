@@ -91,7 +91,7 @@ __global__ __launch_bounds__(64 * kNW) void decode_lds_kernel(
     __shared__ u32x4 L0[kNW][kBlockChunks], L1[kNW][kBlockChunks], L2[kNW][kBlockChunks],
         L3[kNW][kBlockChunks], L4[kNW][kBlockChunks], L5[kNW][kBlockChunks],
         L6[kNW][kBlockChunks], L7[kNW][kBlockChunks];
-    __shared__ float s_rs[32], s_mu[32];
+    __shared__ float s_rs[32], s_mu[32];  // per row: statistics; late RMS: rs (epilogue)
     __shared__ float s_ss[kNW][32];     // late RMS: per-wave sums of x^2 per row
 
     const int tid = threadIdx.x;
@@ -346,9 +346,12 @@ __global__ __launch_bounds__(64 * kNW) void decode_lds_kernel(
     wait_vmcnt<0>();
 
     // Partials: wave w writes its row block nb into its own slot nb as
-    // float [16 n][16 MB m] (1 KB per 16 m, fits the 2 KB slot); late RMS:
-    // the wave's sum of x^2 per row (diagonal element i of a 16x16 result
-    // sits in lane i + 16 (i / 4), accumulator register i % 4).
+    // float [16 MB m][16 n] (1 KB per 16 m, fits the 2 KB slot): lane (lr,
+    // lg) holds n = 4 lg .. 4 lg + 3 of column m = lr, one 16-byte store,
+    // and the epilogue's lanes read consecutive n of one m (no LDS bank
+    // conflicts either way). Late RMS: the wave's sum of x^2 per row
+    // (diagonal element i of a 16x16 result sits in lane i + 16 (i / 4),
+    // accumulator register i % 4).
     if constexpr (LATE) {
         if (lg == (lr >> 2)) {
             const int r = lr & 3;
@@ -360,14 +363,23 @@ __global__ __launch_bounds__(64 * kNW) void decode_lds_kernel(
     }
     static_for<0, NBK>([&](auto NB) {
         constexpr int nb = decltype(NB)::value;
-        float *p = reinterpret_cast<float *>(slot(NB, wave));
+        floatx4 *p = reinterpret_cast<floatx4 *>(slot(NB, wave));
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                p[(lg * 4 + r) * (16 * MB) + mb * 16 + lr] = acc[nb][mb][r];
+            p[(mb * 16 + lr) * 4 + lg] = acc[nb][mb];
     });
     lds_barrier();
+    if constexpr (LATE) {
+        // each row's scale once: sum of the waves' x^2 in wave order
+        if (tid < M) {
+            float q = 0.0f;
+#pragma unroll
+            for (int w = 0; w < kNW; ++w)
+                q += s_ss[w][tid];
+            s_rs[tid] = rsqrtf(q / (float)K + eps);
+        }
+        lds_barrier();
+    }
 
     // Epilogue: sum the 8 partials in wave order, bias, activation, one
     // rounding; thread t of a row block handles n = t % 16, m = t / 16.
@@ -379,14 +391,9 @@ __global__ __launch_bounds__(64 * kNW) void decode_lds_kernel(
             float v = 0.0f;
 #pragma unroll
             for (int w = 0; w < kNW; ++w)
-                v += reinterpret_cast<const float *>(slot(NB, w))[nr * (16 * MB) + m];
-            if constexpr (LATE) {
-                float q = 0.0f;
-#pragma unroll
-                for (int w = 0; w < kNW; ++w)
-                    q += s_ss[w][m];
-                v *= rsqrtf(q / (float)K + eps);
-            }
+                v += reinterpret_cast<const float *>(slot(NB, w))[m * 16 + nr];
+            if constexpr (LATE)
+                v *= s_rs[m];
             if (n < N) {
                 if (bias)
                     v += bits_to_f<DT>(bias[n]);

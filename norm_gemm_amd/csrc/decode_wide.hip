@@ -90,7 +90,7 @@ __global__ __launch_bounds__(64 * kNW) void decode_wide_kernel(
     constexpr int XL = 8 + (HG ? 8 : 0) + (HB ? 8 : 0);  // loads per x group
     constexpr int BL = 8;                          // loads per W block
     __shared__ u32x4 S0[kNW][kSlotChunks], S1[kNW][kSlotChunks];   // 128 KB
-    __shared__ float s_stat[16][2];     // NM_STATS: (rs, mu) per row
+    __shared__ float s_stat[16][2];     // (rs, mu) per row; late RMS: rs (epilogue)
     __shared__ float s_ss[kNW][16];     // NM_RMS_LATE: per-wave sums of x^2
 
     const int tid = threadIdx.x;
@@ -393,8 +393,10 @@ __global__ __launch_bounds__(64 * kNW) void decode_wide_kernel(
     wait_vmcnt<0>();
 
     // Partials: wave w writes row block nb into its own slot 0 as
-    // float [16 n][16 m] at nb * 1 KB (NBK <= 8 blocks fit in 8 KB); late
-    // RMS: the wave's sum of x^2 per row.
+    // float [16 m][16 n] at nb * 1 KB (NBK <= 8 blocks fit in 8 KB): lane
+    // (lr, lg) holds n = 4 lg .. 4 lg + 3 of column m = lr, one 16-byte
+    // store, and the epilogue's lanes read consecutive n of one m (no LDS
+    // bank conflicts either way). Late RMS: the wave's sum of x^2 per row.
     if constexpr (NM == NM_RMS_LATE) {
         // diagonal element i of the 16x16 result sits in lane i + 16 (i / 4),
         // accumulator register i % 4
@@ -404,14 +406,23 @@ __global__ __launch_bounds__(64 * kNW) void decode_wide_kernel(
         }
     }
     {
-        float *p = reinterpret_cast<float *>(S0[wave]);
+        floatx4 *p = reinterpret_cast<floatx4 *>(S0[wave]);
 #pragma unroll
         for (int nb = 0; nb < NBK; ++nb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                p[nb * 256 + (lg * 4 + r) * 16 + lr] = acc[nb][r];
+            p[nb * 64 + lr * 4 + lg] = acc[nb];
     }
     lds_barrier();
+    if constexpr (NM == NM_RMS_LATE) {
+        // each row's scale once: sum of the waves' x^2 in wave order
+        if (tid < M) {
+            float q = 0.0f;
+#pragma unroll
+            for (int w = 0; w < kNW; ++w)
+                q += s_ss[w][tid];
+            s_stat[tid][0] = rsqrtf(q / (float)K + eps);
+        }
+        lds_barrier();
+    }
 
     // Epilogue: sum the 8 partials in wave order, bias, activation, one
     // rounding; thread t handles n = n0 + t % (16 NBK), m = t / (16 NBK).
@@ -421,14 +432,9 @@ __global__ __launch_bounds__(64 * kNW) void decode_wide_kernel(
         float v = 0.0f;
 #pragma unroll
         for (int w = 0; w < kNW; ++w)
-            v += reinterpret_cast<const float *>(S0[w])[(nl >> 4) * 256 + (nl & 15) * 16 + m];
-        if constexpr (NM == NM_RMS_LATE) {
-            float q = 0.0f;
-#pragma unroll
-            for (int w = 0; w < kNW; ++w)
-                q += s_ss[w][m];
-            v *= rsqrtf(q / (float)K + eps);
-        }
+            v += reinterpret_cast<const float *>(S0[w])[(nl >> 4) * 256 + m * 16 + (nl & 15)];
+        if constexpr (NM == NM_RMS_LATE)
+            v *= s_stat[m][0];
         if (n < N) {
             if (bias)
                 v += bits_to_f<DT>(bias[n]);
