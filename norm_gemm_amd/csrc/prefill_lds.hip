@@ -5,27 +5,34 @@
 // computed, aligned contiguous accesses).
 //
 // One workgroup of 8 waves per 128 x 256 output tile, one workgroup per CU
-// (150 KB of LDS). Each wave computes a 64 x 64 block of the tile.
+// (144 KB of LDS: three stages of a 128 x 64 x tile and a 256 x 64 W tile).
+// Each wave computes a 64 x 64 block of the tile.
 //   statistics  a separate pass reduces each row of x once (one pass, fp32
 //               sum and sum of squares) and leaves (1/sigma, -mu/sigma) in
 //               the tile's own rows of y, which the main kernel reads before
 //               it writes them (an in-kernel prologue is used when y cannot
 //               serve as scratch).
-//   K loop      BK = 64, three LDS stages, W loads two steps ahead. W goes
-//               HBM -> LDS by direct 128-bit loads (no registers), one after
-//               each pair of MFMAs so that the load unit stays busy while the
-//               matrix cores run; so does x when it is not normalized. With
-//               normalization each lane loads its x chunks of step k + 1
-//               into registers at the start of step k, normalizes them in its
-//               last sub-step (fp32 arithmetic, one rounding to the operand
-//               type) and writes them once into the next stage, so the normalized x
-//               lives only in registers and LDS. gamma and beta come with x,
-//               or, when both are given, through small LDS slots loaded by
-//               one wave per workgroup two steps ahead.
+//   K loop      BK = 64, three LDS stages, loads two steps ahead. W goes
+//               HBM -> LDS by direct 128-bit loads (no registers); so does x
+//               when it is not normalized. With normalization each lane
+//               loads its x chunks (and its gamma / beta chunk) into
+//               registers two steps ahead, normalizes them between its own
+//               MFMAs of the step before they are needed (fp32 arithmetic,
+//               one rounding to the operand type) and writes them once into
+//               their stage, so the normalized x lives only in registers and
+//               LDS.
+//   schedule    the two waves of each SIMD alternate a memory phase (LDS
+//               fragment reads, load issue) and an MFMA phase, so the matrix
+//               core of every SIMD always has a wave with operands ready
+//               (see the kernel).
 //   gated       (GT) a tile's 256 W rows are the gate and up rows of 128
 //               output columns; the epilogue forms act(gate) * up.
-//   split K     (SK) workgroups split the K steps of a tile in two and write
-//               fp32 partials, summed in order by a second kernel.
+//   split K     (SK) workgroups split the K steps of a tile into ksplit
+//               ranges and write fp32 partials, summed in order by a second
+//               kernel.
+//   folding     (FOLD) W holds gamma folded in, x goes to the MFMAs raw and
+//               the epilogue applies the row statistics and two folded
+//               vectors (see the kernel).
 //   MFMA        v_mfma_f32_32x32x16 with W as the first operand and normalized
 //               x as the second, so each 32x32 result block is y^T: lane l
 //               holds output row m = l % 32 and four consecutive columns.
@@ -187,17 +194,18 @@ __global__ __launch_bounds__(256) void row_stats_to_y_kernel(const uint16_t *__r
 // SIMD (workgroups are dealt to SIMDs that way), and the two groups of four
 // waves alternate between two phases separated by workgroup barriers:
 //   memory phase of step kt: read all of this wave's MFMA fragments of step
-//     kt from LDS into registers; issue the direct loads of step kt + 2;
-//     once the loads of step kt + 1 have landed, normalize this wave's x
-//     chunks of step kt + 1 into their stage and issue the x loads of step
-//     kt + 2 into the same registers;
-//   compute phase of step kt: the 16 MFMAs of step kt, back to back.
+//     kt from LDS into registers; issue the x / gamma / beta register loads
+//     of a later step and (first group) the direct loads of step kt + 2;
+//   compute phase of step kt: the 16 MFMAs of step kt, with this wave's x
+//     chunks of a later step normalized into their stage between them
+//     (second group: the direct loads of step kt + 3 first).
 // Waves 4-7 start one phase later, so while one wave of a SIMD runs its
-// MFMAs the other runs its memory phase (LDS reads, loads, VALU work), and
-// the matrix core of every SIMD always has a wave with operands ready. Each
+// MFMAs the other runs its memory phase (LDS reads, load issue), and the
+// matrix core of every SIMD always has a wave with operands ready. Each
 // stage is read by the first group in phase 2 kt and by the second in phase
 // 2 kt + 1, so a stage is rewritten (direct loads of kt + 3, normalized x of
-// kt + 3) only from phase 2 kt + 2 on.
+// kt + 3) only from phase 2 kt + 2 on. The exact load order and waits are
+// given with the prologue below.
 template <int DT, int STATS, int GB, bool KT, bool GT, bool SK, bool FOLD>
 __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ gamma,

@@ -125,6 +125,25 @@ def test_folded_is_deterministic():
     assert torch.equal(c1, c12) and torch.equal(c2, c22)
 
 
+@pytest.mark.parametrize("norm", [LN, RMS])
+def test_folded_output_columns_do_not_depend_on_n(norm):
+    """The first 256 columns of a 640-column folded call equal a call on those
+    rows of W', c1 and c2 bit for bit (an output element's arithmetic does not
+    depend on N)."""
+    import norm_gemm_amd as ng
+    case = synth.make_norm_gemm(f"folded_onecol_{norm}", 90, 264, 640, norm=norm,
+                                beta=norm == LN, bias=True, eps=1e-5, seed=91 + norm)
+    u, wf, c1, c2 = fold_case(case)
+    c1 = c1 if norm == LN else None
+    y = ng.fused_norm_gemm_folded(u("x"), wf, c1, c2, eps=1e-5, norm=norm)
+    y1 = ng.fused_norm_gemm_folded(u("x"), wf[:256].contiguous(),
+                                   None if c1 is None else c1[:256].contiguous(),
+                                   c2[:256].contiguous(), eps=1e-5, norm=norm)
+    torch.cuda.synchronize()
+    assert_close(to_f64(y), oracle.run_case(case), TOL, case.name)
+    assert torch.equal(y[:, :256].contiguous().view(torch.int16), y1.view(torch.int16))
+
+
 def test_folded_unaligned_is_unsupported():
     import norm_gemm_amd as ng
     case = synth.make_norm_gemm("folded_unaligned", 40, 64, 32, norm=RMS, seed=4)

@@ -395,6 +395,27 @@ def test_stacked_qkv_weight_equals_three_calls(M):
         assert_close(to_f64(joined), to_f64(y), tol=2e-3, what="qkv parts")
 
 
+@pytest.mark.parametrize("norm,beta,dtype", [(LN, True, F16), (RMS, True, F16), (RMS, False, F16),
+                                               (LN, True, BF16), (RMS, False, BF16)])
+def test_output_columns_do_not_depend_on_n(norm, beta, dtype):
+    """The arithmetic of an output element does not depend on N (tile count,
+    statistics records per tile): the first 256 columns of a 768-column call
+    equal a call on those 256 rows of W bit for bit."""
+    import norm_gemm_amd as ng
+    M, K, N = 100, 520, 768
+    case = synth.make_norm_gemm(f"onecol_{norm}{beta}{dtype}", M, K, N, dtype=dtype, norm=norm,
+                                beta=beta, bias=True, eps=1e-5, seed=77 + norm)
+    A = case.arrays
+    u = lambda k: upload(A.get(k), dtype)
+    x, g, b, W, bias = u("x"), u("gamma"), u("beta"), u("W"), u("bias")
+    y = ng.fused_norm_gemm(x, W, g, b, bias, eps=1e-5, norm=norm)
+    y1 = ng.fused_norm_gemm(x, W[:256].contiguous(), g, b, bias[:256].contiguous(), eps=1e-5,
+                            norm=norm)
+    torch.cuda.synchronize()
+    assert_close(to_f64(y), oracle.run_case(case), what="768 columns")
+    assert torch.equal(y[:, :256].contiguous().view(torch.int16), y1.view(torch.int16))
+
+
 @pytest.mark.parametrize("M,K,F,N,dtype", [(100, 264, 520, 136, F16), (300, 512, 2000, 512, BF16),
                                             (64, 136, 200, 72, F16)])
 def test_ffn_split_k_of_the_second_gemm(M, K, F, N, dtype):
