@@ -381,23 +381,42 @@ __global__ __launch_bounds__(64 * kNW) void decode_lds_kernel(
         lds_barrier();
     }
 
-    // Epilogue: sum the 8 partials in wave order, bias, activation, one
-    // rounding; thread t of a row block handles n = t % 16, m = t / 16.
+    // Epilogue: wave w finishes row block nb = w. Lane item (m, q) sums the
+    // 8 partials of outputs n = 4 q .. 4 q + 3 of row m in wave order (16-byte
+    // LDS reads), scales them (late RMS), adds the bias, applies the
+    // activation and rounds once; 8-byte stores where the rows allow them.
+    const bool vst = (N & 3) == 0 && ((uintptr_t)y & 7u) == 0;
     static_for<0, NBK>([&](auto NB) {
         constexpr int nb = decltype(NB)::value;
-        for (int idx = tid; idx < M * 16; idx += 64 * kNW) {
-            const int m = idx >> 4, nr = idx & 15;
-            const int n = n0 + nb * 16 + nr;
-            float v = 0.0f;
+        if (wave != nb)
+            return;
+        for (int idx = lane; idx < M * 4; idx += 64) {
+            const int m = idx >> 2, q = idx & 3;
+            floatx4 v = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int w = 0; w < kNW; ++w)
-                v += reinterpret_cast<const float *>(slot(NB, w))[m * 16 + nr];
-            if constexpr (LATE)
-                v *= s_rs[m];
-            if (n < N) {
-                if (bias)
-                    v += bits_to_f<DT>(bias[n]);
-                y[(int64_t)m * N + n] = f_to_bits<DT>(apply_act(v, act));
+                v += reinterpret_cast<const floatx4 *>(slot(NB, w))[m * 4 + q];
+            const int n = n0 + nb * 16 + 4 * q;
+            uint16_t o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float t = v[e];
+                if constexpr (LATE)
+                    t *= s_rs[m];
+                if (bias && n + e < N)
+                    t += bits_to_f<DT>(bias[n + e]);
+                o[e] = f_to_bits<DT>(apply_act(t, act));
+            }
+            uint16_t *yp = y + (int64_t)m * N + n;
+            if (vst && n + 3 < N) {
+                *reinterpret_cast<uint2 *>(yp) =
+                    make_uint2((uint32_t)o[0] | ((uint32_t)o[1] << 16),
+                               (uint32_t)o[2] | ((uint32_t)o[3] << 16));
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (n + e < N)
+                        yp[e] = o[e];
             }
         }
     });

@@ -424,21 +424,41 @@ __global__ __launch_bounds__(64 * kNW) void decode_wide_kernel(
         lds_barrier();
     }
 
-    // Epilogue: sum the 8 partials in wave order, bias, activation, one
-    // rounding; thread t handles n = n0 + t % (16 NBK), m = t / (16 NBK).
-    for (int idx = tid; idx < M * NBK * 16; idx += 64 * kNW) {
-        const int m = idx / (NBK * 16), nl = idx % (NBK * 16);
-        const int n = n0 + nl;
-        float v = 0.0f;
+    // Epilogue: wave w finishes row block nb = w. Lane item (m, q) sums the
+    // 8 partials of outputs n = 4 q .. 4 q + 3 of row m in wave order (16-byte
+    // LDS reads), scales them (late RMS), adds the bias, applies the
+    // activation and rounds once; 8-byte stores where the rows allow them.
+    const bool vst = (N & 3) == 0 && ((uintptr_t)y & 7u) == 0;
+    if (wave < NBK) {
+        const int nb = wave;
+        for (int idx = lane; idx < M * 4; idx += 64) {
+            const int m = idx >> 2, q = idx & 3;
+            floatx4 v = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int w = 0; w < kNW; ++w)
-            v += reinterpret_cast<const float *>(S0[w])[(nl >> 4) * 256 + m * 16 + (nl & 15)];
-        if constexpr (NM == NM_RMS_LATE)
-            v *= s_stat[m][0];
-        if (n < N) {
-            if (bias)
-                v += bits_to_f<DT>(bias[n]);
-            y[(int64_t)m * N + n] = f_to_bits<DT>(apply_act(v, act));
+            for (int w = 0; w < kNW; ++w)
+                v += reinterpret_cast<const floatx4 *>(S0[w])[nb * 64 + m * 4 + q];
+            const int n = n0 + nb * 16 + 4 * q;
+            uint16_t o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float t = v[e];
+                if constexpr (NM == NM_RMS_LATE)
+                    t *= s_stat[m][0];
+                if (bias && n + e < N)
+                    t += bits_to_f<DT>(bias[n + e]);
+                o[e] = f_to_bits<DT>(apply_act(t, act));
+            }
+            uint16_t *yp = y + (int64_t)m * N + n;
+            if (vst && n + 3 < N) {
+                *reinterpret_cast<uint2 *>(yp) =
+                    make_uint2((uint32_t)o[0] | ((uint32_t)o[1] << 16),
+                               (uint32_t)o[2] | ((uint32_t)o[3] << 16));
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (n + e < N)
+                        yp[e] = o[e];
+            }
         }
     }
 }
