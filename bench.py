@@ -77,7 +77,8 @@ def kernel_sources_sha() -> str:
 def recorded_traffic(workload_name: str):
     """HBM bytes per step measured with rocprofv3 (FETCH_SIZE and WRITE_SIZE,
     scaled by a copy-kernel calibration), or None when no record exists for
-    this workload or the kernels changed since it was taken."""
+    this workload (its name, plus ":folded" for the folded variant) or the
+    kernels changed since it was taken."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path, encoding="utf-8") as f:
@@ -204,7 +205,8 @@ def measure(name: str, steps: int, warmup: int):
         "warmup": warmup,
         "launches_per_step": launches_per_step(case),
         "roofline": {"bound": bound, "achieved": round(value, 1), "peak": peak, "unit": runit,
-                     "frac": round(value / peak, 4), "traffic": recorded_traffic(case.name)},
+                     "frac": round(value / peak, 4),
+                     "traffic": recorded_traffic(case.name + (":folded" if folded else ""))},
         "host_wall_s": round(wall, 4),
         "weight_copies": copies,
     }
@@ -307,7 +309,7 @@ def main():
         "dtype": "f16" if case.dtype == 0 else "bf16",
         "data": "synthetic (seeded PCG64 normals; W rotated over %d device copies)"
                 % main_res["weight_copies"],
-        "config": {"workload": case.name, "M": case.M, "K": case.K, "N": case.N,
+        "config": {"workload": main_res["workload"], "M": case.M, "K": case.K, "N": case.N,
                    **({"F": case.F} if is_ffn else {}),
                    "norm": ["none", "layernorm", "rmsnorm"][case.norm],
                    "act": ["none", "silu", "relu", "gelu"][case.act],

@@ -84,3 +84,29 @@ def test_gemm_norm_rms_invariant_on_gpu():
     y = to_f64(run_case_gpu(case))
     torch.cuda.synchronize()
     assert np.allclose((y * y).mean(axis=1), 1.0, atol=2e-3)
+
+
+@pytest.mark.parametrize("M,N,K,dtype,offset", [(33, 1001, 200, F16, 0), (3, 16400, 72, BF16, 0),
+                                               (70, 2048, 136, F16, 1), (9, 12288, 64, BF16, 0)])
+def test_gemm_norm_row_kernel_forms(M, N, K, dtype, offset):
+    """The row kernel's forms: rows held in registers with 8-byte accesses
+    (N % 4 == 0, N <= 16384), the same with 2-byte accesses (bias, gamma and
+    beta at an odd element offset), N % 4 != 0 and N > 16384 (rows re-read
+    from L2); LayerNorm with every affine term, every output."""
+    import norm_gemm_amd as ng
+    case = synth.make_gemm_norm(f"gemm_norm_form_{M}x{N}x{K}_{offset}", M, K, N, dtype=dtype,
+                                norm=LN, bias=True, gamma=True, beta=True, eps=1e-5, seed=N + K)
+    A = case.arrays
+
+    def vec(k):
+        t = upload(A[k], dtype)
+        if not offset:
+            return t
+        buf = torch.empty(t.numel() + offset, dtype=t.dtype, device=t.device)
+        buf[offset:] = t
+        return buf[offset:]
+
+    y = ng.fused_gemm_norm(upload(A["x"], dtype), upload(A["W"], dtype), vec("bias"),
+                           vec("gamma"), vec("beta"), eps=1e-5, norm=LN)
+    torch.cuda.synchronize()
+    assert_close(to_f64(y), oracle.run_case(case), TOL, case.name)
