@@ -674,27 +674,33 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
                 acc[j][i] = mfma32<DT>(fb[kk][j], fa[kk][i], acc[j][i]);
     };
     // the step's MFMAs; with normalization, x of step kn from buffer r is
-    // normalized into stage As between them (chunk 0 after sub-step 0,
-    // chunk 1 after sub-step 1), so the VALU work issues while the matrix
-    // core runs this wave's MFMAs
+    // normalized into stage As between them, a few VALU instructions after
+    // each MFMA (scheduling groups), so the VALU work issues while the matrix
+    // core runs the MFMAs before it instead of holding the next one back
     auto compute = [&](int kn, u32x4 *As, NormRaw &r) {
-        mfma_kk(0);
-        sb();
         if constexpr (AFFINE) {
+            mfma_kk(0);
             nrm_chunk(kn, As, r, 0);
-            sb();
             mfma_kk(1);
-            sb();
             nrm_chunk(kn, As, r, 1);
+            mfma_kk(2);
+            mfma_kk(3);
+#pragma unroll
+            for (int i = 0; i < 4 * FM * FN; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // up to five VALU
+            }
             sb();
         } else {
+            mfma_kk(0);
+            sb();
             mfma_kk(1);
             sb();
+            mfma_kk(2);
+            sb();
+            mfma_kk(3);
+            sb();
         }
-        mfma_kk(2);
-        sb();
-        mfma_kk(3);
-        sb();
     };
     auto tail_fix = [&](int kt, auto s1) {
         if (KT && kt + 1 == nk - 1) {
