@@ -31,7 +31,7 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
 C_FLAGS = ["-O2", "-std=c11", "-fPIC", "-Wall", "-Wextra", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 SOURCES = ["api.cpp", "prefill.hip", "prefill_lds.hip", "decode.hip", "decode_lds.hip", "decode_wide.hip",
-           "gated.hip", "fold.hip", "postnorm.hip"]
+           "gated.hip", "prefill_wide.hip", "fold.hip", "postnorm.hip"]
 C_SOURCES = ["validate.c", "route.c"]
 
 

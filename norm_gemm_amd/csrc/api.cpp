@@ -80,6 +80,16 @@ ng::GemmArgs make_args(const void *x, const void *gamma, const void *beta, const
     return a;
 }
 
+// 256 x 192 tiles for normalizing calls when they fit the request and move
+// fewer bytes per CU than 128 x 256 tiles, and y can hold the statistics
+// records (N % 8 == 0, 16-byte aligned rows)
+bool wide_tiles(const ng::GemmArgs &a)
+{
+    return a.norm != NG_NORM_NONE && !a.c2 && a.N % 8 == 0 && ((uintptr_t)a.y & 15u) == 0 &&
+           ng_wide_tiles_fit(a.M, a.N, a.K, a.vec ? 1 : 0) &&
+           ng_wide_tiles_pay(a.M, a.N, ng::cu_count());
+}
+
 int run(const ng::GemmArgs &a, hipStream_t s)
 {
     hipError_t e;
@@ -87,7 +97,9 @@ int run(const ng::GemmArgs &a, hipStream_t s)
     case NG_ROUTE_DECODE_ELEM: e = ng::launch_decode(a, s); break;
     case NG_ROUTE_DECODE_WIDE: e = ng::launch_decode_wide(a, s); break;
     case NG_ROUTE_DECODE_LDS: e = ng::launch_decode_lds(a, s); break;
-    case NG_ROUTE_PREFILL_LDS: e = ng::launch_prefill_lds(a, s); break;
+    case NG_ROUTE_PREFILL_LDS:
+        e = wide_tiles(a) ? ng::launch_prefill_wide(a, s) : ng::launch_prefill_lds(a, s);
+        break;
     default: e = ng::launch_prefill(a, s); break;
     }
     return e == hipSuccess ? NG_OK : NG_ERR_HIP;

@@ -28,6 +28,13 @@ hipError_t launch_decode_wide(const GemmArgs &a, hipStream_t s); // route NG_ROU
 // gated tiled kernel: a.W = [W_gate; W_up] is [2 a.N, a.K], a.bias [2 a.N]
 // (only when ng_gated_tiled_fits)
 hipError_t launch_prefill_lds_gated(const GemmArgs &a, hipStream_t s);
+// 256 x 192 tiles for normalizing calls (ng_wide_tiles_fit, no folded
+// weights, N % 8 == 0 and a 16-byte aligned y for the statistics records)
+hipError_t launch_prefill_wide(const GemmArgs &a, hipStream_t s);
+// row statistics (rs, -mu rs) into the first 8 bytes of each row's slice of
+// every tw-column tile of y (tn tiles per row)
+hipError_t launch_row_stats_to_y(const void *x, void *y, int64_t M, int64_t N, int64_t K,
+                                 float eps, int norm, int tn, int tw, int dtype, hipStream_t s);
 // folded weights (a.W = W', a.c1, a.c2; route NG_ROUTE_PREFILL_LDS for any M)
 hipError_t launch_prefill_lds_folded(const GemmArgs &a, hipStream_t s);
 // W' = W * gamma, c1 = W' 1, c2 = W beta + bias (one workgroup per row of W)

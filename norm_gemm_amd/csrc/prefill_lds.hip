@@ -987,6 +987,21 @@ hipError_t launch_dt(const GemmArgs &a, hipStream_t s)
 
 }  // namespace
 
+hipError_t launch_row_stats_to_y(const void *x, void *y, int64_t M, int64_t N, int64_t K,
+                                 float eps, int norm, int tn, int tw, int dtype, hipStream_t s)
+{
+    const dim3 grid((unsigned)((M + 3) / 4)), block(256);
+    if (dtype == DT_F16)
+        hipLaunchKernelGGL((row_stats_to_y_kernel<DT_F16>), grid, block, 0, s,
+                           (const uint16_t *)x, (uint16_t *)y, (int)M, (int)N, (int)K, eps, norm,
+                           tn, tw);
+    else
+        hipLaunchKernelGGL((row_stats_to_y_kernel<DT_BF16>), grid, block, 0, s,
+                           (const uint16_t *)x, (uint16_t *)y, (int)M, (int)N, (int)K, eps, norm,
+                           tn, tw);
+    return hipGetLastError();
+}
+
 hipError_t launch_prefill_lds(const GemmArgs &a, hipStream_t s)
 {
     // tile offsets are 32-bit (see ng_tile_offsets_fit)

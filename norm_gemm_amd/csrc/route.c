@@ -46,3 +46,23 @@ int ng_gated_tiled_fits(int64_t M, int64_t F, int64_t K, int vec)
 {
     return vec && M > NG_DECODE_MAX_M && F >= 1 && ng_tile_offsets_fit(F + NG_TILE_ROWS, K);
 }
+
+int ng_wide_tiles_fit(int64_t M, int64_t N, int64_t K, int vec)
+{
+    return vec && M > NG_DECODE_MAX_M && N >= 1 && K >= 64 && K % 64 == 0 &&
+           ng_tile_offsets_fit(NG_TILE_ROWS, K);
+}
+
+int ng_wide_tiles_pay(int64_t M, int64_t N, int cus)
+{
+    if (M < 1 || N < 1)
+        return 0;
+    if (cus < 1)
+        cus = 256;
+    const int64_t tw = ((M + 255) / 256) * ((N + 191) / 192);
+    const int64_t tn = ((M + 127) / 128) * ((N + 255) / 256);
+    const int64_t rw = (tw + cus - 1) / cus, rn = (tn + cus - 1) / cus;
+    /* bytes per CU: rounds x (256 + 192) rows against rounds x (128 + 256)
+     * rows of 64 elements per K step; the wide tile must save at least 10 % */
+    return rw * 448 * 10 < rn * 384 * 9;
+}

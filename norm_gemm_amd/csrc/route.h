@@ -42,6 +42,17 @@ int ng_route_gemm(int64_t M, int64_t N, int64_t K, int vec, int cus);
  * rows past a tile's first gate row) within 32 bits. */
 int ng_gated_tiled_fits(int64_t M, int64_t F, int64_t K, int vec);
 
+/* 1 when the 256 x 192 tiled kernel can serve the request: aligned, M above
+ * the decode range, K a whole number of 64-element steps, and its x and W
+ * tile offsets (256 rows) within 32 bits. */
+int ng_wide_tiles_fit(int64_t M, int64_t N, int64_t K, int vec);
+
+/* 1 when 256 x 192 tiles move fewer bytes per CU than 128 x 256 tiles over
+ * the whole call on `cus` compute units: rounds of tiles times the bytes of
+ * one 64-element K step of one tile (56 KB against 48 KB). The K step of the
+ * tiled kernels is bound by the L2 bytes a CU can have in flight. */
+int ng_wide_tiles_pay(int64_t M, int64_t N, int cus);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,4 +1,4 @@
-"""The prefill kernel issues its x / gamma / beta register loads as inline asm
+"""The prefill kernels issue their x / gamma / beta register loads as inline asm
 (the compiler does not count them) and hands the destination registers
 through an explicit ``s_waitcnt vmcnt`` statement before any use. The
 hardware writes those registers whenever the load returns, so no instruction
@@ -6,7 +6,7 @@ may read or write them on any path between the load and the next vmcnt
 wait: otherwise a copy would read stale data, or a reused register would be
 overwritten late. This compiles the kernel to gfx950 assembly (no GPU
 needed) and checks that property on every control-flow path of every
-instantiation.
+instantiation of both tiled kernels.
 """
 import os
 import re
@@ -88,12 +88,14 @@ def test_checker_finds_a_planted_hazard():
 
 @pytest.mark.skipif(shutil.which(HIPCC) is None and not os.path.exists(HIPCC),
                     reason="hipcc not available")
-def test_prefill_async_loads_untouched_until_waited(tmp_path):
-    out = tmp_path / "prefill_lds.s"
+@pytest.mark.parametrize("source,kernel", [("prefill_lds.hip", "prefill_lds_kernel"),
+                                           ("prefill_wide.hip", "prefill_wide_kernel")])
+def test_prefill_async_loads_untouched_until_waited(tmp_path, source, kernel):
+    out = tmp_path / (source + ".s")
     cmd = [HIPCC, *nb.HIP_FLAGS, "-x", "hip", "--cuda-device-only", "-S",
-           os.path.join(nb.CSRC, "prefill_lds.hip"), "-o", str(out)]
+           os.path.join(nb.CSRC, source), "-o", str(out)]
     res = subprocess.run(cmd, capture_output=True, text=True)
     assert res.returncode == 0, res.stderr[-2000:]
-    loads, hz = async_load_hazards(out.read_text().splitlines(), "prefill_lds_kernel")
+    loads, hz = async_load_hazards(out.read_text().splitlines(), kernel)
     assert loads > 0
     assert not hz, hz[:5]

@@ -22,6 +22,10 @@ def L():
     lib.ng_decode_wide_row_blocks.restype = ci
     lib.ng_gated_tiled_fits.argtypes = [i64, i64, i64, ci]
     lib.ng_gated_tiled_fits.restype = ci
+    lib.ng_wide_tiles_fit.argtypes = [i64, i64, i64, ci]
+    lib.ng_wide_tiles_fit.restype = ci
+    lib.ng_wide_tiles_pay.argtypes = [i64, i64, ci]
+    lib.ng_wide_tiles_pay.restype = ci
     return lib
 
 
@@ -77,3 +81,31 @@ def test_gated_tiled_fits(L):
     assert L.ng_gated_tiled_fits(32, 28672, 8192, 1) == 0      # decode range
     assert L.ng_gated_tiled_fits(512, 28672, 8192, 0) == 0     # unaligned
     assert L.ng_gated_tiled_fits(512, 2 ** 20, 8192, 1) == 0   # W rows past 2^32 bytes
+
+
+def test_wide_tiles_fit(L):
+    assert L.ng_wide_tiles_fit(512, 49152, 14336, 1) == 1
+    assert L.ng_wide_tiles_fit(512, 49152, 14337, 1) == 0      # K not whole 64-element steps
+    assert L.ng_wide_tiles_fit(512, 49152, 14336, 0) == 0      # unaligned
+    assert L.ng_wide_tiles_fit(32, 49152, 14336, 1) == 0       # decode range
+    assert L.ng_wide_tiles_fit(512, 49152, 8388608, 1) == 0    # tile offsets past 2^32
+
+
+def wide_pays(M, N, cus):
+    """Rounds of tiles times the rows moved per K step (256 + 192 against
+    128 + 256), the wide tiles saving at least 10 %."""
+    tw = -(-M // 256) * -(-N // 192)
+    tn = -(-M // 128) * -(-N // 256)
+    return -(-tw // cus) * 448 * 10 < -(-tn // cus) * 384 * 9
+
+
+@pytest.mark.parametrize("M,N,cus,want", [
+    (512, 49152, 256, 1),     # 512 wide tiles (2 rounds) against 768 (3 rounds)
+    (1024, 8192, 256, 0),     # 172 against 256 tiles: one round each
+    (512, 14336, 256, 0),     # 150 against 224: one round each
+    (512, 8192, 256, 0),
+    (129, 32776, 256, 1), (300, 21768, 256, 1), (400, 16392, 256, 1),
+    (512, 49152, 304, 1), (512, 49152, 0, 1)])
+def test_wide_tiles_pay(L, M, N, cus, want):
+    assert L.ng_wide_tiles_pay(M, N, cus) == want
+    assert wide_pays(M, N, cus if cus > 0 else 256) == bool(want)
