@@ -92,3 +92,19 @@ def test_wide_tiles_deterministic():
     y2 = ng.fused_norm_gemm(u("x"), u("W"), u("gamma"), eps=1e-6, norm=RMS, act="silu")
     torch.cuda.synchronize()
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+@pytest.mark.parametrize("norm,dtype", [(RMS, F16), (LN, BF16)])
+def test_ffn_first_gemm_on_wide_tiles(norm, dtype):
+    """An FFN with a normalization prologue and a wide hidden layer: its first
+    GEMM (x[300,128] W1[21768,128]) takes the 256 x 192 tiles, writing h and
+    its statistics records into the workspace; every output of y against
+    the oracle."""
+    M, K, F, N = 300, 128, 21768, 256
+    assert routes_wide(M, F, K)
+    case = synth.make_ffn(f"ffn_wide_{norm}_{dtype}", M, K, F, N, dtype=dtype, norm=norm,
+                          act=SILU, gamma=True, beta=norm == LN, b1=True, b2=True, seed=31)
+    from helpers import run_case_gpu
+    y = run_case_gpu(case)
+    torch.cuda.synchronize()
+    assert_close(to_f64(y), oracle.run_case(case), TOL, case.name)
