@@ -149,7 +149,11 @@ def measure(name: str, steps: int, warmup: int):
     out = torch.empty(case.M, case.N, dtype=up["x"].dtype, device=dev)
     ws = None
     if is_ffn:
-        ws = torch.empty(ws_size(case.M, case.F, up["x"].dtype), dtype=torch.uint8, device=dev)
+        # the plain FFN's workspace also holds the two fp32 partial sums of y
+        # that the second GEMM's split K writes (the gated FFN's holds them)
+        extra = 8 * case.M * case.N if case.kind == "ffn" else 0
+        ws = torch.empty(ws_size(case.M, case.F, up["x"].dtype) + extra, dtype=torch.uint8,
+                         device=dev)
     elif case.kind == "gemm_norm":
         ws = torch.empty(2 * ng.fused_gemm_norm_workspace_size(case.M, case.N),
                          dtype=torch.uint8, device=dev)

@@ -109,9 +109,12 @@ int fused_norm_gemm(const void *x, const void *gamma, const void *beta,
  * fused_ffn_workspace_size(M, F, dtype) bytes, 256-byte aligned recommended).
  * A workspace of at least fused_ffn_workspace_size(M, F, dtype) + 8 M N bytes
  * also holds two fp32 partial sums of y: when the second GEMM's 128 x 256
- * tiles fill at most half of the compute units (and M > 32, aligned), its K
- * is then split over two workgroups per tile and the partials are added in a
- * fixed order (deterministic) by a second kernel. Every workspace byte the
+ * tiles (M > 32, aligned) leave compute units idle, its K is then split over
+ * two workgroups per tile and the partials are added in a fixed order
+ * (deterministic) by a second kernel. Tiles on at most half of the CUs take
+ * two equal K ranges; tiles on more than half but not all of them (their
+ * column blocks a multiple of 8, as many on each XCD) keep one workgroup per
+ * tile that skips one slice of K steps, which the spare CUs compute. Every workspace byte the
  * call may touch is checked against the inputs and y (NG_ERR_ALIAS).
  * All kernels (the statistics pass when normalizing with M > 32, the two
  * GEMMs, the partial sum when K is split) run on `stream`, in order, without
@@ -207,7 +210,7 @@ int fused_norm_gemm_folded(const void *x, const void *W_folded, const float *c1,
  * are kept in fp32 in the workspace (a 16-byte aligned device buffer of at
  * least fused_gemm_norm_workspace_size(M, N) = 4 M N bytes rounded up to 256;
  * twice that lets the GEMM split K over two workgroups per tile when its
- * tiles fill at most half of the CUs); a second kernel adds the bias, takes
+ * tiles leave CUs idle, as in fused_ffn); a second kernel adds the bias, takes
  * the row statistics in two passes and writes y rounded once. Two kernels
  * on `stream`, no synchronization. x and W must be 16-byte aligned with K % 8
  * == 0 and K <= 8,388,600 (the tiled kernel, any M), else NG_ERR_UNSUPPORTED.

@@ -184,7 +184,10 @@ def fused_ffn(x: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor,
     """y = act(norm_affine(x) @ w1[F, K].T + b1) @ w2[N, F].T + b2.
 
     The intermediate h[M, F] lives in ``workspace`` (a uint8 device tensor of
-    at least :func:`fused_ffn_workspace_size` bytes; allocated when not given).
+    at least :func:`fused_ffn_workspace_size` bytes). 8 M N bytes more also
+    hold two fp32 partial sums of y, which lets the second GEMM split K when
+    its tiles leave CUs idle; the workspace allocated when none is given has
+    that room.
     """
     return _ffn(False, x, w1, w2, gamma, beta, b1, b2, eps, norm, act, workspace, out, stream)
 
@@ -239,7 +242,10 @@ def _ffn(gated, x, w1, w2, gamma, beta, b1, b2, eps, norm, act, workspace, out, 
     if not noalloc:
         need = (fused_gated_ffn_workspace_size if gated else fused_ffn_workspace_size)(M, F, x.dtype)
         if workspace is None:
-            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+            # plain FFN: room for the two fp32 partial sums of y past h (the
+            # gated FFN's [gate | up] area already holds them when F >= 2 N)
+            workspace = torch.empty(need + (0 if gated else 8 * M * N), dtype=torch.uint8,
+                                    device=dev)
         if workspace.device != dev or not workspace.is_contiguous():
             raise ValueError("workspace must be a contiguous tensor on x's device")
     lead = tuple(x.shape[:-1])

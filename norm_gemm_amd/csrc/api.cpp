@@ -105,10 +105,12 @@ int run(const ng::GemmArgs &a, hipStream_t s)
     return e == hipSuccess ? NG_OK : NG_ERR_HIP;
 }
 
-// Second GEMM of an FFN: y = h . W2^T + b2. When its tiles fill at most
-// half of the CUs and the workspace past h holds two fp32 partial sums of y,
-// K is split over two workgroups per tile and the partials are added in a
-// fixed order by a second kernel.
+// Second GEMM of an FFN: y = h . W2^T + b2. When the workspace past h holds
+// two fp32 partial sums of y and the tiles leave CUs idle, K is split over
+// two workgroups per tile (tiles on at most half of the CUs: two equal
+// ranges; on more than half: the skipped-slice schedule of
+// ng_skip_slice_plan), and the two partials are added in a fixed order by a
+// second kernel.
 int ffn_down(const void *h, const void *W2, const void *b2, void *y, int64_t M, int64_t F,
              int64_t N, int dtype, void *workspace, size_t workspace_bytes, hipStream_t s)
 {
@@ -119,10 +121,15 @@ int ffn_down(const void *h, const void *W2, const void *b2, void *y, int64_t M, 
     const size_t pbytes = 2u * (size_t)M * (size_t)N * 4u;
     char *part = (char *)workspace + hbytes;
     if (ng_route_gemm(M, N, F, a.vec ? 1 : 0, cus) == NG_ROUTE_PREFILL_LDS &&
-        2 * ng::prefill_tiles(M, N) <= cus &&
-        ng::prefill_k_steps(F) >= 4 && workspace_bytes >= hbytes + pbytes &&
-        ((uintptr_t)part & 15u) == 0) {
-        if (ng::launch_prefill_lds_splitk(a, (float *)part, 2, s) != hipSuccess ||
+        workspace_bytes >= hbytes + pbytes && ((uintptr_t)part & 15u) == 0) {
+        hipError_t e = hipErrorInvalidValue;
+        if (2 * ng::prefill_tiles(M, N) <= cus && ng::prefill_k_steps(F) >= 4)
+            e = ng::launch_prefill_lds_splitk(a, (float *)part, 2, s);
+        else if (ng_skip_slice_plan(M, N, F, cus, nullptr, nullptr))
+            e = ng::launch_prefill_lds_skip_slice(a, (float *)part, s);
+        else
+            return run(a, s);
+        if (e != hipSuccess ||
             ng::launch_splitk_sum((const float *)part, b2, y, M, N, 2, NG_ACT_NONE, dtype, s) !=
                 hipSuccess)
             return NG_ERR_HIP;
@@ -242,16 +249,20 @@ int fused_gemm_norm(const void *x, const void *W, const void *bias, const void *
         NG_ROUTE_PREFILL_LDS)
         return NG_ERR_UNSUPPORTED;
     hipStream_t s = (hipStream_t)stream;
-    // K split over two workgroups per tile when the tiles fill at most half of
-    // the CUs and the workspace holds two planes
+    // K split over two workgroups per tile when the workspace holds two
+    // planes and the tiles leave CUs idle: two equal ranges when the tiles
+    // fill at most half of the CUs, else the skipped-slice schedule
     const size_t plane = ng_gemm_norm_workspace_size(M, N);
-    const int ksplit = (2 * ng::prefill_tiles(M, N) <= ng::cu_count() &&
-                        ng::prefill_k_steps(K) >= 4 && workspace_bytes >= 2 * plane)
-                           ? 2
-                           : 1;
-    // the planes are M N floats apart: with ksplit 2 the partial of range s
+    const int cus = ng::cu_count();
+    const bool two = workspace_bytes >= 2 * plane;
+    const bool halves = two && 2 * ng::prefill_tiles(M, N) <= cus && ng::prefill_k_steps(K) >= 4;
+    const bool skip = two && !halves && ng_skip_slice_plan(M, N, K, cus, nullptr, nullptr);
+    const int ksplit = halves || skip ? 2 : 1;
+    // the planes are M N floats apart: with ksplit 2 the partial of part s
     // starts at s M N (the sum kernel's layout), inside the two planes
-    if (ng::launch_prefill_lds_splitk(a, (float *)workspace, ksplit, s) != hipSuccess ||
+    const hipError_t e = skip ? ng::launch_prefill_lds_skip_slice(a, (float *)workspace, s)
+                              : ng::launch_prefill_lds_splitk(a, (float *)workspace, ksplit, s);
+    if (e != hipSuccess ||
         ng::launch_postnorm((const float *)workspace, bias, gamma, beta, y, M, N, ksplit, eps,
                             norm, dtype, s) != hipSuccess)
         return NG_ERR_HIP;

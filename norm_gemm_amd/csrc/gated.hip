@@ -50,11 +50,70 @@ __global__ __launch_bounds__(256) void splitk_sum_kernel(const float *__restrict
     }
 }
 
+// The same sum, eight consecutive outputs of one row per thread (N % 8 == 0,
+// part and y 16-byte aligned): two 16-byte loads per plane, one 16-byte
+// store. Threads map to 8-column chunks of a row (x) and rows (y, strided),
+// so the bias chunk is read once per thread and no index is divided.
+template <int DT>
+__global__ __launch_bounds__(256) void splitk_sum_vec_kernel(const float *__restrict__ part,
+                                                             const uint16_t *__restrict__ bias,
+                                                             uint16_t *__restrict__ y, int64_t M,
+                                                             int64_t N, int ksplit, int act)
+{
+    const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;   // 8-column chunk
+    if (c * 8 >= N)
+        return;
+    const int64_t n = c * 8, plane = M * N;
+    float b[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        b[e] = 0.0f;
+    if (bias) {
+        const uint4 bv = *reinterpret_cast<const uint4 *>(bias + n);
+        const uint32_t w[4] = {bv.x, bv.y, bv.z, bv.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            b[e] = bits_to_f<DT>((uint16_t)((w[e >> 1] >> ((e & 1) * 16)) & 0xffffu));
+    }
+    for (int64_t m = blockIdx.y; m < M; m += gridDim.y) {
+        const float *p = part + m * N + n;
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            v[e] = 0.0f;
+        for (int s = 0; s < ksplit; ++s) {
+            const float4 lo = *reinterpret_cast<const float4 *>(p + s * plane);
+            const float4 hi = *reinterpret_cast<const float4 *>(p + s * plane + 4);
+            v[0] += lo.x; v[1] += lo.y; v[2] += lo.z; v[3] += lo.w;
+            v[4] += hi.x; v[5] += hi.y; v[6] += hi.z; v[7] += hi.w;
+        }
+        uint32_t o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t a = f_to_bits<DT>(apply_act(v[2 * e] + b[2 * e], act));
+            const uint32_t h = f_to_bits<DT>(apply_act(v[2 * e + 1] + b[2 * e + 1], act));
+            o[e] = a | (h << 16);
+        }
+        *reinterpret_cast<uint4 *>(y + m * N + n) = uint4{o[0], o[1], o[2], o[3]};
+    }
+}
+
 }  // namespace
 
 hipError_t launch_splitk_sum(const float *part, const void *bias, void *y, int64_t M, int64_t N,
                              int ksplit, int act, int dtype, hipStream_t s)
 {
+    if (N % 8 == 0 && ((uintptr_t)part & 15u) == 0 && ((uintptr_t)y & 15u) == 0 &&
+        ((uintptr_t)bias & 15u) == 0) {
+        const dim3 grid((unsigned)((N / 8 + 255) / 256), (unsigned)(M < 4096 ? M : 4096));
+        if (dtype == DT_F16)
+            hipLaunchKernelGGL((splitk_sum_vec_kernel<DT_F16>), grid, dim3(256), 0, s, part,
+                               (const uint16_t *)bias, (uint16_t *)y, M, N, ksplit, act);
+        else
+            hipLaunchKernelGGL((splitk_sum_vec_kernel<DT_BF16>), grid, dim3(256), 0, s, part,
+                               (const uint16_t *)bias, (uint16_t *)y, M, N, ksplit, act);
+        return hipGetLastError();
+    }
     const int64_t blocks64 = (M * N + 255) / 256;
     const unsigned blocks = (unsigned)(blocks64 < 16384 ? blocks64 : 16384);
     if (dtype == DT_F16)

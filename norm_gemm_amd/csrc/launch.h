@@ -46,6 +46,10 @@ hipError_t launch_fold(const void *W, const void *gamma, const void *beta, const
 int prefill_tiles(int64_t M, int64_t N);
 int prefill_k_steps(int64_t K);
 hipError_t launch_prefill_lds_splitk(const GemmArgs &a, float *part, int ksplit, hipStream_t s);
+// Plain GEMM on the skipped-slice schedule of ng_skip_slice_plan (fp32
+// partials of the two parts of every tile in planes 0 and 1 of part, M N
+// floats apart); hipErrorInvalidValue when the plan does not apply.
+hipError_t launch_prefill_lds_skip_slice(const GemmArgs &a, float *part, hipStream_t s);
 hipError_t launch_splitk_sum(const float *part, const void *bias, void *y, int64_t M, int64_t N,
                              int ksplit, int act, int dtype, hipStream_t s);
 // y = norm_affine(sum of the partials + bias) over each output row

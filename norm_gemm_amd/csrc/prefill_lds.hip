@@ -28,7 +28,9 @@
 //   gated       (GT) a tile's 256 W rows are the gate and up rows of 128
 //               output columns; the epilogue forms act(gate) * up.
 //   split K     (SK) workgroups split the K steps of a tile into ksplit
-//               ranges and write fp32 partials, summed in order by a second
+//               ranges, or (skipped slice) one workgroup per tile skips one
+//               slice of K steps that a spare workgroup computes; each part
+//               is written as fp32 partials, summed in order by a second
 //               kernel.
 //   folding     (FOLD) W holds gamma folded in, x goes to the MFMAs raw and
 //               the epilogue applies the row statistics and two folded
@@ -97,6 +99,8 @@ __device__ __forceinline__ floatx16 mfma32(const u32x4 &a, const u32x4 &b, const
 struct TileMap {
     int tm, tn, T;      // row blocks, column blocks, tiles
     int xcd;            // 1: XCD-grouped assignment (see file comment)
+    int tails, len;     // skipped-slice split K: spare workgroups per XCD and
+                        // slice length in K steps (tails 0: not used)
 };
 
 // Tile of workgroup b (one tile per workgroup, T workgroups). XCD-grouped:
@@ -178,10 +182,10 @@ __global__ __launch_bounds__(256) void row_stats_to_y_kernel(const uint16_t *__r
 // GB: bit 0 gamma present, bit 1 beta present (with STATS != ST_NONE);
 // KT: K % 64 != 0 (the last K step is ragged); GT: gated output (see the
 // gated epilogue): W is [2N, K] = [W_gate; W_up], bias [2N], and a tile
-// covers 128 output columns; SK: split K (no normalization): workgroup b
-// computes tile b % T over the b / T-th of ksplit contiguous K ranges and
-// writes its fp32 partial sums to part[b / T][M][N] (bias and activation are
-// applied by the sum of the partials). norm selects LayerNorm or RMSNorm for
+// covers 128 output columns; SK: split K (no normalization): the tile's K
+// range is one part of its K steps (the kernel below says which) and its fp32
+// partial sums go to one plane part[p][M][N] (bias and activation are applied
+// by the sum of the partials). norm selects LayerNorm or RMSNorm for
 // the in-kernel statistics (STATS == ST_PROLOGUE). FOLD: inference-mode
 // folding (page "LayerNorm 融合算子如何让大模型推理再快 15%？深度拆解 ATB 的实现",
 // section 6.2, tip 2): W holds W' = W * gamma, x goes to the MFMAs unnormalized
@@ -206,13 +210,18 @@ __global__ __launch_bounds__(256) void row_stats_to_y_kernel(const uint16_t *__r
 // 2 kt + 1, so a stage is rewritten (direct loads of kt + 3, normalized x of
 // kt + 3) only from phase 2 kt + 2 on. The exact load order and waits are
 // given with the prologue below.
+//
+// One output tile (row block mb, column block nt) over Ke elements of K from
+// kbase; with split K its fp32 sums go to plane `plane` of part, and K steps
+// gap_at on are taken gap_len steps further on (a skipped slice).
 template <int DT, int STATS, int GB, bool KT, bool GT, bool SK, bool FOLD>
-__global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
+__device__ __forceinline__ void prefill_tile(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ gamma,
     const uint16_t *__restrict__ beta, const uint16_t *__restrict__ W,
     const uint16_t *__restrict__ bias, uint16_t *__restrict__ y, int M, int N, int K,
-    float eps, int norm, int act, TileMap mp, int vec_out, float *__restrict__ part, int ksplit,
-    const float *__restrict__ c1, const float *__restrict__ c2)
+    float eps, int norm, int act, int vec_out, float *__restrict__ part,
+    const float *__restrict__ c1, const float *__restrict__ c2, int mb, int nt, int kbase,
+    int Ke, int plane, int gap_at, int gap_len)
 {
     static_assert(!SK || (STATS == ST_NONE && !GT), "split K only for the plain GEMM");
     static_assert(!FOLD || (STATS == ST_FROM_Y || STATS == ST_PROLOGUE) && !GT && !SK && GB == 0,
@@ -263,20 +272,12 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WGN, wn = wave % WGN;   // wm is also the phase group
     const int lrow = lane & 31, lk = lane >> 5;
-    // K range of this workgroup: all of K, or with split K the ks-th of
-    // ksplit ranges of whole K steps (the host gives every range a step).
-    // Ke is the extent of the range; K stays the row stride.
-    const int ks = SK ? (int)blockIdx.x / mp.T : 0;
-    const int nks = SK ? ((K + BK - 1) / BK + ksplit - 1) / ksplit : 0;
-    const int kbase = SK ? ks * nks * BK : 0;
-    const int Ke = SK ? min(K - kbase, nks * BK) : K;
+    // K range of this tile: Ke elements from kbase (K stays the row stride)
     const int nk = (Ke + BK - 1) / BK;
 
     // output columns per tile: 256, or 128 gated (the 256 W rows of a tile are
     // the gate and up rows of the same 128 columns)
     constexpr int BNO = GT ? BN / 2 : BN;
-    int mb, nt;
-    tile_of(mp, SK ? (int)blockIdx.x % mp.T : (int)blockIdx.x, mb, nt);
     const int m0 = mb * BM, n0 = nt * BNO;
 
     // ---- direct HBM -> LDS loads. Instruction i of a wave fills 8 tile rows
@@ -332,8 +333,9 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
     auto issue_dma = [&](int kt, u32x4 *As, u32x4 *Bs) {
         kt = min(kt, nk - 1);
         const bool tl = KT && kt == nk - 1;
-        const char *wb = reinterpret_cast<const char *>(wtile) + (size_t)kt * (BK * 2);
-        const char *xb = reinterpret_cast<const char *>(xtile) + (size_t)kt * (BK * 2);
+        const int kg = SK && kt >= gap_at ? kt + gap_len : kt;   // step within K
+        const char *wb = reinterpret_cast<const char *>(wtile) + (size_t)kg * (BK * 2);
+        const char *xb = reinterpret_cast<const char *>(xtile) + (size_t)kg * (BK * 2);
         if constexpr (!AFFINE) {
 #pragma unroll
             for (int i = 0; i < A_DMA; ++i)
@@ -785,7 +787,7 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
     if constexpr (SK) {
         // ---- split-K epilogue: fp32 partials straight from the accumulators,
         // four consecutive columns (16 bytes) per lane and 32x32 block row
-        float *pp = part + (size_t)ks * M * N;
+        float *pp = part + (size_t)plane * M * N;
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
@@ -919,8 +921,69 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
     }
 }
 
+// Workgroup b computes one tile over the whole K, except with split K (SK):
+//   uniform (mp.tails == 0): tile b % T over the b / T-th of ksplit
+//     contiguous K ranges of whole steps, partial sums to plane b / T;
+//   skipped slice (mp.tails > 0, tn % 8 == 0): on XCD b % 8 the j-th
+//     workgroup (j = b / 8) with j < T / 8 computes local tile j (the
+//     XCD-grouped tile order) over all K steps but those of slot j / tails
+//     (steps [slot len, slot len + len)) into plane 0; workgroup T / 8 + e
+//     computes, for slot i = 0, 1, ..., the skipped slice of local tile
+//     i tails + e into plane 1. The workgroups that skip a slice at a given
+//     slot run it at the same time as the spare workgroups, which so read
+//     the same x steps as the tiles that have not reached their own slice.
+template <int DT, int STATS, int GB, bool KT, bool GT, bool SK, bool FOLD>
+__global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ gamma,
+    const uint16_t *__restrict__ beta, const uint16_t *__restrict__ W,
+    const uint16_t *__restrict__ bias, uint16_t *__restrict__ y, int M, int N, int K,
+    float eps, int norm, int act, TileMap mp, int vec_out, float *__restrict__ part, int ksplit,
+    const float *__restrict__ c1, const float *__restrict__ c2)
+{
+    const int b = blockIdx.x;
+    int nseg = 1;                 // tiles (segments) of this workgroup
+    if constexpr (SK) {
+        if (mp.tails > 0 && (b >> 3) >= (mp.T >> 3))
+            nseg = (mp.T >> 3) / mp.tails;
+    }
+    for (int sg = 0; sg < nseg; ++sg) {
+        int mb, nt, kbase = 0, Ke = K, plane = 0, gap_at = 1 << 30, gap_len = 0;
+        if constexpr (SK) {
+            if (mp.tails > 0) {
+                const int xc = b & 7, j = b >> 3, tx = mp.T >> 3;
+                const int u = j < tx ? j : sg * mp.tails + (j - tx);   // local tile
+                mb = u % mp.tm;
+                nt = xc * (mp.tn >> 3) + u / mp.tm;
+                if (j < tx) {
+                    Ke = K - mp.len * BK;
+                    gap_at = (u / mp.tails) * mp.len;
+                    gap_len = mp.len;
+                } else {
+                    kbase = sg * mp.len * BK;
+                    Ke = mp.len * BK;
+                    plane = 1;
+                }
+            } else {
+                // every range gets at least one step (checked by the host)
+                const int ks = b / mp.T;
+                const int nks = ((K + BK - 1) / BK + ksplit - 1) / ksplit;
+                kbase = ks * nks * BK;
+                Ke = min(K - kbase, nks * BK);
+                plane = ks;
+                tile_of(mp, b % mp.T, mb, nt);
+            }
+        } else {
+            tile_of(mp, b, mb, nt);
+        }
+        prefill_tile<DT, STATS, GB, KT, GT, SK, FOLD>(x, gamma, beta, W, bias, y, M, N, K, eps,
+                                                       norm, act, vec_out, part, c1, c2, mb, nt,
+                                                       kbase, Ke, plane, gap_at, gap_len);
+    }
+}
+
 template <int DT, int STATS, int GB, bool KT, bool GT, bool SK = false, bool FOLD = false>
-hipError_t launch_k(const GemmArgs &a, hipStream_t s, float *part = nullptr, int ksplit = 1)
+hipError_t launch_k(const GemmArgs &a, hipStream_t s, float *part = nullptr, int ksplit = 1,
+                    int tails = 0, int len = 0)
 {
     const int cus = cu_count();
     constexpr int BNO = GT ? BN / 2 : BN;
@@ -929,6 +992,8 @@ hipError_t launch_k(const GemmArgs &a, hipStream_t s, float *part = nullptr, int
     mp.tn = (int)((a.N + BNO - 1) / BNO);
     mp.T = mp.tm * mp.tn;
     mp.xcd = (cus % 8 == 0 && mp.tn % 8 == 0) ? 1 : 0;
+    mp.tails = tails;
+    mp.len = len;
     const int vec_out = (a.N % 8 == 0 && ((uintptr_t)a.y & 15u) == 0) ? 1 : 0;
     if constexpr (STATS == ST_FROM_Y || STATS == ST_FROM_Y_PS) {
         hipLaunchKernelGGL((row_stats_to_y_kernel<DT>), dim3((unsigned)((a.M + 3) / 4)), dim3(256),
@@ -938,7 +1003,8 @@ hipError_t launch_k(const GemmArgs &a, hipStream_t s, float *part = nullptr, int
         if (e != hipSuccess)
             return e;
     }
-    hipLaunchKernelGGL((prefill_lds_kernel<DT, STATS, GB, KT, GT, SK, FOLD>), dim3(mp.T * ksplit),
+    const int grid = tails > 0 ? mp.T + 8 * tails : mp.T * ksplit;
+    hipLaunchKernelGGL((prefill_lds_kernel<DT, STATS, GB, KT, GT, SK, FOLD>), dim3(grid),
                        dim3(THREADS), 0, s,
                        (const uint16_t *)a.x, (const uint16_t *)a.gamma, (const uint16_t *)a.beta,
                        (const uint16_t *)a.W, (const uint16_t *)a.bias, (uint16_t *)a.y, (int)a.M,
@@ -1036,6 +1102,28 @@ hipError_t launch_prefill_lds_splitk(const GemmArgs &a, float *part, int ksplit,
                   : launch_k<DT_F16, ST_NONE, 0, false, false, true>(a, s, part, ksplit);
     return kt ? launch_k<DT_BF16, ST_NONE, 0, true, false, true>(a, s, part, ksplit)
               : launch_k<DT_BF16, ST_NONE, 0, false, false, true>(a, s, part, ksplit);
+}
+
+hipError_t launch_prefill_lds_skip_slice(const GemmArgs &a, float *part, hipStream_t s)
+{
+    // the host plan assumes 128 x 256 tiles of 64-element K steps
+    static_assert(BM == 128 && BN == 256 && BK == 64, "tile shape of the skipped-slice plan");
+    int tails = 0, len = 0;
+    const int cus = cu_count();
+    if (ng_route_gemm(NG_DECODE_MAX_M + 1, a.N, a.K, a.vec ? 1 : 0, cus) != NG_ROUTE_PREFILL_LDS ||
+        a.norm != NORM_NONE || !ng_skip_slice_plan(a.M, a.N, a.K, cus, &tails, &len))
+        return hipErrorInvalidValue;
+    // every workgroup's tiles exist: T / 8 tiles per XCD in whole slots
+    const int T = prefill_tiles(a.M, a.N);
+    if (T % 8 != 0 || (T / 8) % tails != 0 || ((a.N + BN - 1) / BN) % 8 != 0 ||
+        (int64_t)(T / 8 / tails + 1) * len > prefill_k_steps(a.K))
+        return hipErrorInvalidValue;
+    const bool kt = a.K % BK != 0;
+    if (a.dtype == DT_F16)
+        return kt ? launch_k<DT_F16, ST_NONE, 0, true, false, true>(a, s, part, 2, tails, len)
+                  : launch_k<DT_F16, ST_NONE, 0, false, false, true>(a, s, part, 2, tails, len);
+    return kt ? launch_k<DT_BF16, ST_NONE, 0, true, false, true>(a, s, part, 2, tails, len)
+              : launch_k<DT_BF16, ST_NONE, 0, false, false, true>(a, s, part, 2, tails, len);
 }
 
 hipError_t launch_prefill_lds_folded(const GemmArgs &a, hipStream_t s)

@@ -66,3 +66,28 @@ int ng_wide_tiles_pay(int64_t M, int64_t N, int cus)
      * rows of 64 elements per K step; the wide tile must save at least 10 % */
     return rw * 448 * 10 < rn * 384 * 9;
 }
+
+int ng_skip_slice_plan(int64_t M, int64_t N, int64_t K, int cus, int *tails, int *len)
+{
+    if (M < 1 || N < 1 || K < 1 || cus < 8 || cus % 8 != 0)
+        return 0;
+    const int64_t tm = (M + 127) / 128, tn = (N + 255) / 256, T = tm * tn;
+    if (tn % 8 != 0 || 2 * T <= cus || T >= cus)
+        return 0;
+    const int64_t tx = T / 8, spare = cus / 8 - tx;
+    int64_t e = spare < tx ? spare : tx;
+    while (tx % e != 0)
+        --e;
+    const int64_t slots = tx / e, nkt = (K + 63) / 64;
+    /* a spare workgroup's step takes about 1.1 times a main workgroup's
+     * (its x steps are shared with fewer workgroups, and each slice starts
+     * and drains its own pipeline): (nkt - l) = 1.1 slots l */
+    const int64_t l = (100 * nkt) / (100 + 110 * slots);
+    if (l < 8)
+        return 0;
+    if (tails)
+        *tails = (int)e;
+    if (len)
+        *len = (int)l;
+    return 1;
+}

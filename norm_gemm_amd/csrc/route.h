@@ -53,6 +53,19 @@ int ng_wide_tiles_fit(int64_t M, int64_t N, int64_t K, int vec);
  * tiled kernels is bound by the L2 bytes a CU can have in flight. */
 int ng_wide_tiles_pay(int64_t M, int64_t N, int cus);
 
+/* Skipped-slice schedule of a plain GEMM (no normalization) whose 128 x 256
+ * tiles fill more than half but not all of the CUs in one round: T tiles
+ * with T / 8 on each of the 8 XCDs (tn % 8 == 0, cus % 8 == 0, cus / 2 < T <
+ * cus). On each XCD, every tile keeps its own workgroup, which skips one
+ * slice of `len` K steps (the slice of the tile's slot, see the kernel); the
+ * XCD's `tails` spare workgroups compute the skipped slices, T / 8 / tails
+ * slots one after another, so every tile ends with two fp32 partial sums.
+ * tails is the largest divisor of T / 8 that the spare CUs hold, and len
+ * balances the spare workgroups (slots x len steps, each taking about 1.1
+ * times a main workgroup's step) against the others (K steps - len). Returns 1 and
+ * sets *tails and *len when the schedule applies (len >= 8), else 0. */
+int ng_skip_slice_plan(int64_t M, int64_t N, int64_t K, int cus, int *tails, int *len);
+
 #ifdef __cplusplus
 }
 #endif

@@ -72,3 +72,13 @@ def tile_indices(n: int, tile: int, seed: int, interior: int = 1):
         if b1 > b0 + 1 and interior:
             out.update(int(v) for v in rng.integers(b0 + 1, b1, size=interior))
     return sorted(out)
+
+
+def one_ulp(dtype) -> float:
+    """Bound of |a - b| / (|b| + 1) for two outputs that differ only in the
+    fp32 summation order of the same products (a split K against an unsplit
+    one): each is rounded once to the output type, so they may differ by one
+    unit in the last place, 2^-10 |y| in fp16 and 2^-7 |y| in bf16 (plus a
+    margin for the fp32 sums themselves)."""
+    import synth
+    return (2.0 ** -10 if dtype == synth.F16 else 2.0 ** -7) + 1e-4

@@ -14,7 +14,8 @@ import torch
 
 import oracle
 import synth
-from helpers import TOL, assert_close, run_case_gpu, tdtype, tile_indices, to_f64, upload
+from helpers import (TOL, assert_close, one_ulp, run_case_gpu, tdtype, tile_indices, to_f64,
+                     upload)
 
 pytestmark = pytest.mark.gpu
 
@@ -433,12 +434,13 @@ def test_ffn_split_k_of_the_second_gemm(M, K, F, N, dtype):
     big = torch.empty(need + 8 * M * N + 4096, dtype=torch.uint8, device="cuda")
     y1 = ng.fused_ffn(*args, eps=1e-5, norm=LN, act="silu", workspace=big)
     y2 = ng.fused_ffn(*args, eps=1e-5, norm=LN, act="silu", workspace=big)
-    y0 = ng.fused_ffn(*args, eps=1e-5, norm=LN, act="silu")
+    small = torch.empty(need, dtype=torch.uint8, device="cuda")    # h only: unsplit
+    y0 = ng.fused_ffn(*args, eps=1e-5, norm=LN, act="silu", workspace=small)
     torch.cuda.synchronize()
     ref = oracle.run_case(case)
     assert_close(to_f64(y1), ref, what=case.name)
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
-    assert_close(to_f64(y1), to_f64(y0), tol=5e-3, what="split vs unsplit")
+    assert_close(to_f64(y1), to_f64(y0), tol=one_ulp(dtype), what="split vs unsplit")
 
 
 @pytest.mark.parametrize("M", [16, 100])
@@ -448,8 +450,11 @@ def test_ffn_equals_two_norm_gemm_calls(M):
                           b1=True, b2=True, seed=13)
     A = case.arrays
     u = lambda k: upload(A[k], F16)
+    # a workspace that holds h only: the second GEMM is one unsplit call
+    ws = torch.empty(ng.fused_ffn_workspace_size(M, 320, torch.float16), dtype=torch.uint8,
+                     device="cuda")
     y = ng.fused_ffn(u("x"), u("W1"), u("W2"), u("gamma"), u("beta"), u("b1"), u("b2"),
-                     eps=1e-5, norm=LN, act="silu")
+                     eps=1e-5, norm=LN, act="silu", workspace=ws)
     h = ng.fused_norm_gemm(u("x"), u("W1"), u("gamma"), u("beta"), u("b1"), eps=1e-5, norm=LN,
                            act="silu")
     y2 = ng.fused_norm_gemm(h, u("W2"), bias=u("b2"), norm=NONE)

@@ -26,6 +26,8 @@ def L():
     lib.ng_wide_tiles_fit.restype = ci
     lib.ng_wide_tiles_pay.argtypes = [i64, i64, ci]
     lib.ng_wide_tiles_pay.restype = ci
+    lib.ng_skip_slice_plan.argtypes = [i64, i64, i64, ci, ctypes.POINTER(ci), ctypes.POINTER(ci)]
+    lib.ng_skip_slice_plan.restype = ci
     return lib
 
 
@@ -109,3 +111,104 @@ def wide_pays(M, N, cus):
 def test_wide_tiles_pay(L, M, N, cus, want):
     assert L.ng_wide_tiles_pay(M, N, cus) == want
     assert wide_pays(M, N, cus if cus > 0 else 256) == bool(want)
+
+
+def skip_plan(L, M, N, K, cus):
+    t, ln = ctypes.c_int(0), ctypes.c_int(0)
+    ok = L.ng_skip_slice_plan(M, N, K, cus, ctypes.byref(t), ctypes.byref(ln))
+    return (t.value, ln.value) if ok else None
+
+
+def skip_slice_segments(M, N, K, tails, ln):
+    """The segments of every workgroup of the skipped-slice split K, as the
+    tiled kernel derives them from its workgroup index: (workgroup, row block,
+    column block, plane, list of K steps). Workgroups are dealt to the 8 XCDs
+    round-robin; the j-th of XCD xc with j < T / 8 owns local tile j and skips
+    the len steps of slot j // tails; the others run the skipped slices of
+    local tiles i tails + (j - T / 8), slot i after slot i."""
+    tm, tn, nkt = -(-M // 128), -(-N // 256), -(-K // 64)
+    T = tm * tn
+    tx = T // 8
+    segs = []
+    for b in range(T + 8 * tails):
+        xc, j = b % 8, b // 8
+        units = [j] if j < tx else [i * tails + j - tx for i in range(tx // tails)]
+        for sg, u in enumerate(units):
+            mb, nt = u % tm, xc * (tn // 8) + u // tm
+            if j < tx:
+                gap_at = (u // tails) * ln
+                nk = nkt - ln
+                steps = [kt + ln if kt >= gap_at else kt for kt in range(nk)]
+                segs.append((b, mb, nt, 0, steps))
+            else:
+                segs.append((b, mb, nt, 1, list(range(sg * ln, sg * ln + ln))))
+    return segs
+
+
+@pytest.mark.parametrize("M,N,K,cus,want", [
+    (512, 14336, 49152, 256, (4, 88)),     # FFN second GEMM: 224 tiles, 768 K steps
+    (512, 14336, 14336, 256, (4, 25)),
+    (512, 12288, 49152, 256, (8, 178)),    # 192 tiles: 24 per XCD, 8 spare CUs each, 3 slots
+    (300, 12288, 1792, 256, (9, 8)),       # 144 tiles (ragged rows): 18 per XCD, 9 of 14 spare CUs used
+    (512, 14336, 4096, 256, None),         # 64 K steps: slices under 8 steps
+    (512, 8192, 49152, 256, None),         # 128 tiles: half of the CUs, two equal ranges instead
+    (1024, 8192, 8192, 256, None),         # 256 tiles fill the CUs
+    (512, 13824, 49152, 256, None),        # 54 column blocks, not a multiple of 8
+    (512, 14336, 49152, 240, (2, 46)),     # 224 tiles on 240 CUs: 2 spare per XCD, 14 slots
+    (512, 14336, 49152, 0, None),
+])
+def test_skip_slice_plan(L, M, N, K, cus, want):
+    assert skip_plan(L, M, N, K, cus) == want
+
+
+@pytest.mark.parametrize("M,N,K,cus", [
+    (512, 14336, 49152, 256), (512, 14336, 14336, 256), (512, 12288, 49152, 256),
+    (300, 12288, 1792, 256), (300, 12288, 1800, 256), (129, 18432, 3000, 256),
+    (640, 8192, 5000, 256), (512, 14336, 49152, 240), (200, 20480, 20000, 304),
+])
+def test_skip_slice_segments_cover_every_step_once(L, M, N, K, cus):
+    """Every (tile, K step) is computed by exactly one segment; every tile has
+    one part in plane 0 and one in plane 1 (the two planes the sum kernel
+    adds); every step index is inside K and only the main parts hold the
+    last (possibly ragged) step; the grid fits the CUs."""
+    plan = skip_plan(L, M, N, K, cus)
+    assert plan is not None, (M, N, K, cus)
+    tails, ln = plan
+    tm, tn, nkt = -(-M // 128), -(-N // 256), -(-K // 64)
+    T = tm * tn
+    assert cus // 2 < T < cus and tn % 8 == 0 and (T // 8) % tails == 0
+    assert T + 8 * tails <= cus
+    assert (T // 8 // tails + 1) * ln <= nkt          # the launcher's check
+    cover = {}
+    planes = {}
+    for b, mb, nt, plane, steps in skip_slice_segments(M, N, K, tails, ln):
+        assert 0 <= mb < tm and 0 <= nt < tn
+        assert len(steps) >= 1 and all(0 <= k < nkt for k in steps)
+        assert len(set(steps)) == len(steps)
+        if plane == 1:
+            assert nkt - 1 not in steps and steps == list(range(steps[0], steps[0] + ln))
+        for k in steps:
+            cover[(mb, nt, k)] = cover.get((mb, nt, k), 0) + 1
+        planes.setdefault((mb, nt), []).append(plane)
+    assert len(cover) == T * nkt and set(cover.values()) == {1}
+    assert len(planes) == T and all(sorted(p) == [0, 1] for p in planes.values())
+
+
+def test_skip_slice_spare_workgroups_run_the_slot_being_skipped(L):
+    """At slot i the spare workgroups of an XCD compute exactly the slices
+    that the XCD's tiles of slot i skip, and those are the same K steps for
+    every tile of the slot (so the spare and the skipping workgroups read the
+    same steps of x at about the same time)."""
+    M, N, K = 512, 14336, 49152
+    tails, ln = skip_plan(L, M, N, K, 256)
+    segs = skip_slice_segments(M, N, K, tails, ln)
+    tx = 224 // 8
+    for xc in range(8):
+        spare = [s for s in segs if s[0] % 8 == xc and s[0] // 8 >= tx]
+        main = [s for s in segs if s[0] % 8 == xc and s[0] // 8 < tx]
+        for i in range(tx // tails):
+            at_slot = {(s[1], s[2]) for s in spare if s[4][0] == i * ln}
+            skipping = {(s[1], s[2]) for s in main if (s[0] // 8) // tails == i}
+            assert at_slot == skipping and len(at_slot) == tails
+            # the tiles of a slot share their W column block (tails = row blocks)
+            assert len({nt for _, nt in at_slot}) == 1
