@@ -112,10 +112,26 @@ def algorithmic(case):
 
 
 def launches_per_step(case) -> int:
+    """Kernel launches of one step (aligned shapes, workspace with room for
+    the split-K partials): a statistics pass before a normalizing GEMM with
+    M > 32; the FFN's second GEMM split over K (its partial sum is a second
+    launch) when its 128 x 256 tiles leave CUs idle."""
     if case.kind == "gemm_norm":
         return 2
-    is_ffn = case.kind in ("ffn", "gated_ffn")
-    return (2 if is_ffn else 1) + (1 if case.norm and case.M > 32 else 0)
+    first = 1 + (1 if case.norm and case.M > 32 else 0)
+    if case.kind not in ("ffn", "gated_ffn"):
+        return first
+    import ctypes
+    import torch
+    import norm_gemm_amd as ng
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    lib = ng.lib
+    lib.ng_skip_slice_plan.argtypes = [ctypes.c_int64] * 3 + [ctypes.c_int, ctypes.c_void_p,
+                                                              ctypes.c_void_p]
+    tiles = -(-case.M // 128) * -(-case.N // 256)
+    split = case.M > 32 and ((2 * tiles <= cus and -(-case.F // 64) >= 4) or
+                             lib.ng_skip_slice_plan(case.M, case.N, case.F, cus, None, None))
+    return first + (2 if split else 1)
 
 
 def measure(name: str, steps: int, warmup: int):
