@@ -286,8 +286,17 @@ int fused_gated_ffn(const void *x, const void *gamma, const void *beta, const vo
     hipStream_t s = (hipStream_t)stream;
     char *h = (char *)workspace;
     // phase 1: h = act(a . W_gate^T + b_gate) * (a . W_up^T + b_up)
-    const ng::GemmArgs a = make_args(x, gamma, beta, W1, b1, h, M, F, K, eps, norm, act, dtype);
+    ng::GemmArgs a = make_args(x, gamma, beta, W1, b1, h, M, F, K, eps, norm, act, dtype);
     if (ng_gated_tiled_fits(M, F, K, a.vec ? 1 : 0)) {
+        // the [gate | up] area past h (unused by the tiled kernel, and inside
+        // the size the validation checked) holds the partial sums of the
+        // last round's split tiles, if any
+        const size_t hbytes = (((size_t)M * (size_t)F * 2u) + 255u) & ~(size_t)255u;
+        const size_t need = ng_gated_ffn_workspace_size(M, F, dtype);
+        if (need > hbytes) {
+            a.part = (float *)((char *)workspace + hbytes);
+            a.part_bytes = need - hbytes;
+        }
         if (ng::launch_prefill_lds_gated(a, s) != hipSuccess)
             return NG_ERR_HIP;
     } else {

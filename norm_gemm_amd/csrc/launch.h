@@ -18,6 +18,10 @@ struct GemmArgs {
     bool vec;  // K % 8 == 0 and x, W, gamma, beta 16-byte aligned
     // inference-mode folding: W holds W' = W * gamma; c1 = W' 1, c2 = W beta + bias
     const float *c1 = nullptr, *c2 = nullptr;
+    // gated calls: device scratch (16-byte aligned) for the fp32 partial sums
+    // of the last round's tiles when their K is split (ng_gated_split_tiles)
+    float *part = nullptr;
+    size_t part_bytes = 0;
 };
 
 hipError_t launch_prefill(const GemmArgs &a, hipStream_t s);      // any alignment

@@ -101,6 +101,8 @@ struct TileMap {
     int xcd;            // 1: XCD-grouped assignment (see file comment)
     int tails, len;     // skipped-slice split K: spare workgroups per XCD and
                         // slice length in K steps (tails 0: not used)
+    int split_from;     // gated: workgroups from this index on compute K halves
+                        // of the last tiles (split_from = T: none)
 };
 
 // Tile of workgroup b (one tile per workgroup, T workgroups). XCD-grouped:
@@ -484,8 +486,8 @@ __device__ __forceinline__ void prefill_tile(
 #pragma unroll
         for (int i = 0; i < A_DMA; ++i)
             r.v[i] = ldg16_async(xb, tl ? aoff_t[i] : aoff_g[i]);
-        const char *gb = reinterpret_cast<const char *>(gamma) + (size_t)kt * (BK * 2);
-        const char *bb = reinterpret_cast<const char *>(beta) + (size_t)kt * (BK * 2);
+        const char *gb = reinterpret_cast<const char *>(gamma) + (size_t)(kbase + kt * BK) * 2;
+        const char *bb = reinterpret_cast<const char *>(beta) + (size_t)(kbase + kt * BK) * 2;
         if constexpr (HG)
             r.g = ldg16_async(gb, tl ? goff_t : goff);
         else
@@ -812,6 +814,25 @@ __device__ __forceinline__ void prefill_tile(
         return;
     }
     if constexpr (GT) {
+        if (plane >= 0) {
+            // ---- a K half of a split tile: the fp32 gate (j = 0) and up
+            // (j = 1) sums times the row factor, stored as the tile's block
+            // [128 rows][gate 128 | up 128] (no bias, no activation)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int nl = wn * 32 + q * 8 + lk * 4;
+#pragma unroll
+                for (int i = 0; i < FM; ++i) {
+                    const int ml = wm * WM + i * 32 + lrow;
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        *reinterpret_cast<floatx4 *>(part + ml * 256 + j * 128 + nl) =
+                            floatx4{acc[j][i][q * 4] * osc[i], acc[j][i][q * 4 + 1] * osc[i],
+                                    acc[j][i][q * 4 + 2] * osc[i], acc[j][i][q * 4 + 3] * osc[i]};
+                }
+            }
+            return;
+        }
         // ---- gated epilogue: each lane holds the gate (j = 0) and up (j = 1)
         // sums of the same output elements; h = act(gate + b_gate) *
         // (up + b_up) in fp32, one rounding, staged row-major in B0 (128 rows
@@ -947,7 +968,10 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
             nseg = (mp.T >> 3) / mp.tails;
     }
     for (int sg = 0; sg < nseg; ++sg) {
-        int mb, nt, kbase = 0, Ke = K, plane = 0, gap_at = 1 << 30, gap_len = 0;
+        // plane: the partial-sum plane of a split K (every split path sets
+        // it), -1 for a whole tile
+        int mb, nt, kbase = 0, Ke = K, plane = -1, gap_at = 1 << 30, gap_len = 0;
+        float *pt = part;
         if constexpr (SK) {
             if (mp.tails > 0) {
                 const int xc = b & 7, j = b >> 3, tx = mp.T >> 3;
@@ -958,6 +982,7 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
                     Ke = K - mp.len * BK;
                     gap_at = (u / mp.tails) * mp.len;
                     gap_len = mp.len;
+                    plane = 0;
                 } else {
                     kbase = sg * mp.len * BK;
                     Ke = mp.len * BK;
@@ -972,12 +997,66 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_lds_kernel(
                 plane = ks;
                 tile_of(mp, b % mp.T, mb, nt);
             }
+        } else if (GT && b >= mp.split_from) {
+            // gated, last round: workgroup split_from + 2 s + h computes K half
+            // h of tile split_from + s (first half: the first ceil(nkt / 2)
+            // steps) into plane h of that tile's partial block
+            const int hw = b - mp.split_from, st = hw >> 1, S = mp.T - mp.split_from;
+            tile_of(mp, mp.split_from + st, mb, nt);
+            const int k1 = ((K + BK - 1) / BK + 1) / 2 * BK;
+            kbase = (hw & 1) ? k1 : 0;
+            Ke = (hw & 1) ? K - k1 : k1;
+            plane = hw & 1;
+            pt = part + ((size_t)plane * S + st) * (BM * 256);
         } else {
             tile_of(mp, b, mb, nt);
         }
         prefill_tile<DT, STATS, GB, KT, GT, SK, FOLD>(x, gamma, beta, W, bias, y, M, N, K, eps,
-                                                       norm, act, vec_out, part, c1, c2, mb, nt,
+                                                       norm, act, vec_out, pt, c1, c2, mb, nt,
                                                        kbase, Ke, plane, gap_at, gap_len);
+    }
+}
+
+// The gated outputs of the split tiles from the two partial blocks of each:
+// h = act(g0 + g1 + b_gate) * (u0 + u1 + b_up) in fp32, the halves added in
+// order, one rounding. Workgroup 16 s + g covers rows 8 g .. 8 g + 7 of split
+// tile s (tile split_from + s); each thread four consecutive outputs of one
+// row, stored as one 8-byte write when they are whole and aligned.
+template <int DT>
+__global__ __launch_bounds__(256) void gated_split_sum_kernel(const float *__restrict__ part,
+                                                              const uint16_t *__restrict__ bias,
+                                                              uint16_t *__restrict__ h, int M,
+                                                              int F, int act, TileMap mp)
+{
+    const int st = blockIdx.x >> 4, S = mp.T - mp.split_from;
+    int mb, nt;
+    tile_of(mp, mp.split_from + st, mb, nt);
+    const int r = (blockIdx.x & 15) * 8 + (threadIdx.x >> 5), c = (threadIdx.x & 31) * 4;
+    const int m = mb * BM + r, n0 = nt * 128 + c;
+    if (m >= M || n0 >= F)
+        return;
+    const float *p0 = part + (size_t)st * (BM * 256) + r * 256 + c;
+    const float *p1 = part + ((size_t)S + st) * (BM * 256) + r * 256 + c;
+    const floatx4 g0 = *reinterpret_cast<const floatx4 *>(p0);
+    const floatx4 g1 = *reinterpret_cast<const floatx4 *>(p1);
+    const floatx4 u0 = *reinterpret_cast<const floatx4 *>(p0 + 128);
+    const floatx4 u1 = *reinterpret_cast<const floatx4 *>(p1 + 128);
+    uint32_t o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int n = n0 + q;
+        const bool ok = n < F;
+        const float bg = (bias && ok) ? bits_to_f<DT>(bias[n]) : 0.0f;
+        const float bu = (bias && ok) ? bits_to_f<DT>(bias[F + n]) : 0.0f;
+        const float g = (g0[q] + g1[q]) + bg, u = (u0[q] + u1[q]) + bu;
+        o[q] = f_to_bits<DT>(apply_act(g, act) * u);
+    }
+    uint16_t *dst = h + (int64_t)m * F + n0;
+    if (n0 + 4 <= F && ((uintptr_t)dst & 7u) == 0) {
+        *reinterpret_cast<uint2 *>(dst) = make_uint2(o[0] | (o[1] << 16), o[2] | (o[3] << 16));
+    } else {
+        for (int q = 0; q < 4 && n0 + q < F; ++q)
+            dst[q] = (uint16_t)o[q];
     }
 }
 
@@ -994,6 +1073,20 @@ hipError_t launch_k(const GemmArgs &a, hipStream_t s, float *part = nullptr, int
     mp.xcd = (cus % 8 == 0 && mp.tn % 8 == 0) ? 1 : 0;
     mp.tails = tails;
     mp.len = len;
+    mp.split_from = mp.T;
+    // gated: the last round's tiles in two K halves when it holds at most half
+    // of the CUs and the caller's scratch holds their partial sums
+    int nsplit = 0;
+    if constexpr (GT) {
+        nsplit = ng_gated_split_tiles(a.M, a.N, a.K, cus);
+        if (nsplit > 0 && a.part && ((uintptr_t)a.part & 15u) == 0 &&
+            (size_t)nsplit * (BM * 256) * 2 * sizeof(float) <= a.part_bytes) {
+            mp.split_from = mp.T - nsplit;
+            part = a.part;
+        } else {
+            nsplit = 0;
+        }
+    }
     const int vec_out = (a.N % 8 == 0 && ((uintptr_t)a.y & 15u) == 0) ? 1 : 0;
     if constexpr (STATS == ST_FROM_Y || STATS == ST_FROM_Y_PS) {
         hipLaunchKernelGGL((row_stats_to_y_kernel<DT>), dim3((unsigned)((a.M + 3) / 4)), dim3(256),
@@ -1003,13 +1096,23 @@ hipError_t launch_k(const GemmArgs &a, hipStream_t s, float *part = nullptr, int
         if (e != hipSuccess)
             return e;
     }
-    const int grid = tails > 0 ? mp.T + 8 * tails : mp.T * ksplit;
+    const int grid = tails > 0 ? mp.T + 8 * tails : mp.T * ksplit + nsplit;
     hipLaunchKernelGGL((prefill_lds_kernel<DT, STATS, GB, KT, GT, SK, FOLD>), dim3(grid),
                        dim3(THREADS), 0, s,
                        (const uint16_t *)a.x, (const uint16_t *)a.gamma, (const uint16_t *)a.beta,
                        (const uint16_t *)a.W, (const uint16_t *)a.bias, (uint16_t *)a.y, (int)a.M,
                        (int)a.N, (int)a.K, a.eps, a.norm, a.act, mp, vec_out, part, ksplit, a.c1,
                        a.c2);
+    if constexpr (GT) {
+        if (nsplit > 0) {
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess)
+                return e;
+            hipLaunchKernelGGL((gated_split_sum_kernel<DT>), dim3(16 * nsplit), dim3(256), 0, s,
+                               (const float *)part, (const uint16_t *)a.bias, (uint16_t *)a.y,
+                               (int)a.M, (int)a.N, a.act, mp);
+        }
+    }
     return hipGetLastError();
 }
 

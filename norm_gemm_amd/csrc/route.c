@@ -91,3 +91,14 @@ int ng_skip_slice_plan(int64_t M, int64_t N, int64_t K, int cus, int *tails, int
         *len = (int)l;
     return 1;
 }
+
+int ng_gated_split_tiles(int64_t M, int64_t F, int64_t K, int cus)
+{
+    if (M < 1 || F < 1 || K < 1 || cus < 2)
+        return 0;
+    const int64_t T = ((M + 127) / 128) * ((F + 127) / 128);
+    if (T <= cus || (K + 63) / 64 < 4)
+        return 0;
+    const int64_t last = T % cus;
+    return (last > 0 && 2 * last <= cus) ? (int)last : 0;
+}

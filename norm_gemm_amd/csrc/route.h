@@ -66,6 +66,15 @@ int ng_wide_tiles_pay(int64_t M, int64_t N, int cus);
  * sets *tails and *len when the schedule applies (len >= 8), else 0. */
 int ng_skip_slice_plan(int64_t M, int64_t N, int64_t K, int cus, int *tails, int *len);
 
+/* Tiles of the gated tiled kernel's last round whose K steps are split over
+ * two workgroups: T = ceil(M / 128) ceil(F / 128) tiles on `cus` CUs take
+ * more than one round, and when the last round holds at most cus / 2 tiles
+ * each of them is computed as two halves of its K steps (at least 4 steps),
+ * so that the last round takes half the time. Returns that tile count, or 0.
+ * The partial sums take 262144 bytes per split tile (two fp32 planes of
+ * 128 rows x 256 gate and up columns). */
+int ng_gated_split_tiles(int64_t M, int64_t F, int64_t K, int cus);
+
 #ifdef __cplusplus
 }
 #endif

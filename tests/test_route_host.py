@@ -28,6 +28,8 @@ def L():
     lib.ng_wide_tiles_pay.restype = ci
     lib.ng_skip_slice_plan.argtypes = [i64, i64, i64, ci, ctypes.POINTER(ci), ctypes.POINTER(ci)]
     lib.ng_skip_slice_plan.restype = ci
+    lib.ng_gated_split_tiles.argtypes = [i64, i64, i64, ci]
+    lib.ng_gated_split_tiles.restype = ci
     return lib
 
 
@@ -212,3 +214,46 @@ def test_skip_slice_spare_workgroups_run_the_slot_being_skipped(L):
             assert at_slot == skipping and len(at_slot) == tails
             # the tiles of a slot share their W column block (tails = row blocks)
             assert len({nt for _, nt in at_slot}) == 1
+
+
+@pytest.mark.parametrize("M,F,K,cus,want", [
+    (512, 28672, 8192, 256, 128),   # SwiGLU 512 x 28672: 896 tiles, last round 128 of 256
+    (512, 9216, 320, 256, 32),      # 288 tiles
+    (300, 11500, 264, 256, 14),     # 3 row blocks x 90 column blocks = 270 tiles
+    (512, 12288, 8192, 256, 128),   # 384 tiles: the last round exactly half of the CUs
+    (512, 14336, 8192, 256, 0),     # 448 tiles: last round 192 > 128
+    (512, 16384, 8192, 256, 0),     # 512 tiles: two whole rounds
+    (512, 8192, 8192, 256, 0),      # 256 tiles: one round
+    (512, 28672, 192, 256, 0),      # 3 K steps: halves under 2 steps
+    (512, 28672, 8192, 0, 0),
+])
+def test_gated_split_tiles(L, M, F, K, cus, want):
+    assert L.ng_gated_split_tiles(M, F, K, cus) == want
+
+
+def test_gated_split_covers_every_tile_and_step_once(L):
+    """The gated kernel's workgroups (T - S whole tiles, then the two K halves
+    of each of the last S tiles) compute every K step of every tile exactly
+    once, each half at least two steps, and fit one round of the CUs."""
+    for M, F, K, cus in [(512, 28672, 8192, 256), (512, 9216, 320, 256), (300, 11500, 264, 256),
+                         (129, 20000, 1000, 240)]:
+        T = -(-M // 128) * -(-F // 128)
+        S = L.ng_gated_split_tiles(M, F, K, cus)
+        nkt = -(-K // 64)
+        if S == 0:
+            continue
+        assert 2 * S <= cus and S <= T - cus
+        first = T - S
+        cover = {}
+        for b in range(T + S):
+            if b < first:
+                tile, steps = b, range(nkt)
+            else:
+                hw = b - first
+                k1 = (nkt + 1) // 2
+                tile = first + hw // 2
+                steps = range(k1, nkt) if hw & 1 else range(0, k1)
+                assert len(steps) >= 2
+            for k in steps:
+                cover[(tile, k)] = cover.get((tile, k), 0) + 1
+        assert len(cover) == T * nkt and set(cover.values()) == {1}
