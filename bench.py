@@ -115,7 +115,8 @@ def launches_per_step(case) -> int:
     """Kernel launches of one step (aligned shapes, workspace with room for
     the split-K partials): a statistics pass before a normalizing GEMM with
     M > 32; the FFN's second GEMM split over K (its partial sum is a second
-    launch) when its 128 x 256 tiles leave CUs idle."""
+    launch) when its 128 x 256 tiles leave CUs idle; the gated GEMM's split
+    last round (one more launch for its sum)."""
     if case.kind == "gemm_norm":
         return 2
     first = 1 + (1 if case.norm and case.M > 32 else 0)
@@ -126,6 +127,10 @@ def launches_per_step(case) -> int:
     import norm_gemm_amd as ng
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     lib = ng.lib
+    if case.kind == "gated_ffn" and case.M > 32:
+        # the gated GEMM's last round in K halves adds the sum of their partials
+        lib.ng_gated_split_tiles.argtypes = [ctypes.c_int64] * 3 + [ctypes.c_int]
+        first += 1 if lib.ng_gated_split_tiles(case.M, case.F, case.K, cus) > 0 else 0
     lib.ng_skip_slice_plan.argtypes = [ctypes.c_int64] * 3 + [ctypes.c_int, ctypes.c_void_p,
                                                               ctypes.c_void_p]
     tiles = -(-case.M // 128) * -(-case.N // 256)
