@@ -143,9 +143,13 @@ int fused_ffn(const void *x, const void *gamma, const void *beta,
  * projection); b1, when given, is [2F] in the same order. act = SiLU gives
  * SwiGLU. For M > 32 with 16-byte aligned operands and K % 8 == 0, phase 1
  * is one tiled kernel whose tiles hold the gate and up rows of the same
- * output columns, so g and u meet in registers and only h is written. Else
- * the [gate | up] projections of every row go to the workspace and a second
- * kernel forms h. The workspace must hold fused_gated_ffn_workspace_size(M,
+ * output columns, so g and u meet in registers and only h is written; when
+ * those 128 x 128-column tiles take more than one round of the compute units
+ * and the last round holds at most half of them, each tile of that round is
+ * computed as two halves of its K steps whose fp32 sums go to the workspace
+ * past h (262144 bytes per tile, within the size below) and a small kernel
+ * forms h for those tiles (fixed order, deterministic). Else the [gate | up]
+ * projections of every row go to the workspace and a second kernel forms h. The workspace must hold fused_gated_ffn_workspace_size(M,
  * F, dtype) bytes (3 M F elements: h, then the [M, 2F] projections); other
  * conventions as fused_ffn, including the split K of the second GEMM, whose
  * partials (8 M N bytes after the 256-byte-rounded h) fit in this size when

@@ -1078,6 +1078,8 @@ hipError_t launch_k(const GemmArgs &a, hipStream_t s, float *part = nullptr, int
     // of the CUs and the caller's scratch holds their partial sums
     int nsplit = 0;
     if constexpr (GT) {
+        // the host plan counts 128 x 128-column gated tiles of 64-element steps
+        static_assert(BM == 128 && BNO == 128 && BK == 64, "tile shape of the gated split plan");
         nsplit = ng_gated_split_tiles(a.M, a.N, a.K, cus);
         if (nsplit > 0 && a.part && ((uintptr_t)a.part & 15u) == 0 &&
             (size_t)nsplit * (BM * 256) * 2 * sizeof(float) <= a.part_bytes) {
