@@ -218,6 +218,18 @@ __device__ __forceinline__ void dma16(const void *sbase, uint32_t voff, uint32_t
                  : "memory", "m0");
 }
 
+// The same direct load with the non-temporal hint: the L2 may replace the
+// lines first. For operand tiles with few readers (each W line of a 256-row
+// tile is read by the two workgroups of its column block and then never
+// again), so that the lines other workgroups still share stay resident.
+__device__ __forceinline__ void dma16_nt(const void *sbase, uint32_t voff, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+                 :
+                 : "v"(voff), "s"(sbase), "s"(lds)
+                 : "memory", "m0");
+}
+
 // The same direct load with a per-lane 64-bit address (lanes may read from
 // different arrays); inactive lanes neither read nor write LDS.
 __device__ __forceinline__ void dma16_ptr(const void *p, uint32_t lds)

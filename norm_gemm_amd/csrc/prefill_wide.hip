@@ -168,7 +168,7 @@ __global__ __launch_bounds__(THREADS, 1) void prefill_wide_kernel(
         const char *wb = reinterpret_cast<const char *>(wtile) + (size_t)kt * (BK * 2);
 #pragma unroll
         for (int i = 0; i < B_DMA; ++i)
-            dma16(wb, woff[i], lds_addr(&Bs[(wave * B_RPW + i * 8) * CPR]));
+            dma16_nt(wb, woff[i], lds_addr(&Bs[(wave * B_RPW + i * 8) * CPR]));
     };
 
     // row statistics: of this lane's x rows (normalization) and of the
