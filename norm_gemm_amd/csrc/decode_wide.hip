@@ -37,6 +37,11 @@
 namespace ng {
 namespace {
 
+// Cache policy of the W loads: non-temporal (nt), so the L2 may replace the
+// streamed W lines first; every W line is read once per call, and the hint
+// keeps them from crowding the L2 (M = 32: 82.6 -> 74.7 us on W[28672, 8192]).
+constexpr int kWPolicy = 2;
+
 constexpr int kNW = 8;                   // waves per workgroup
 constexpr int kNBMax = 8;                // max 16-row blocks of W per workgroup
 constexpr int kSlotChunks = 16 * 32;     // 16 rows x 32 chunks of 16 bytes = 8 KB
@@ -153,7 +158,7 @@ __global__ __launch_bounds__(64 * kNW) void decode_wide_kernel(
             const int k = kb * kKB + (lchunk ^ (2 * q)) * 8;
             __builtin_amdgcn_global_load_lds(
                 (const void *)(wb + (int64_t)(2 * q) * K + (lrowoff + (k < K ? k : 0))),
-                (__attribute__((address_space(3))) void *)&dst[q * 64], 16, 0, 0);
+                (__attribute__((address_space(3))) void *)&dst[q * 64], 16, 0, kWPolicy);
         }
     };
 
