@@ -26,7 +26,10 @@
 //               core of every SIMD always has a wave with operands ready
 //               (see the kernel).
 //   gated       (GT) a tile's 256 W rows are the gate and up rows of 128
-//               output columns; the epilogue forms act(gate) * up.
+//               output columns; the epilogue forms act(gate) * up. When the
+//               tiles take more than one round and the last holds at most
+//               half of the CUs, that round's tiles run as two K halves whose
+//               fp32 gate / up sums a small kernel combines.
 //   split K     (SK) workgroups split the K steps of a tile into ksplit
 //               ranges, or (skipped slice) one workgroup per tile skips one
 //               slice of K steps that a spare workgroup computes; each part
